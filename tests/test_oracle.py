@@ -1,0 +1,344 @@
+"""Pins of the oracle against facts fixed outside the oracle itself.
+
+Each test names what it pins: values the pages print, closed forms, hand-computed examples,
+brute force on tiny shapes, algebraic invariants of the TP decomposition, and the format tables.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import layout, linear, numerics, shapes
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------------------------
+# Storage-format decoders
+# ---------------------------------------------------------------------------------------------
+
+def test_bf16_decode_known_patterns():
+    # IEEE binary32 upper halves: 1.0, -2.0, +inf, smallest subnormal, largest finite, 0.5
+    bits = np.array([0x3F80, 0xC000, 0x7F80, 0x0001, 0x7F7F, 0x3F00], dtype=np.uint16)
+    v = numerics.bf16_bits_to_f64(bits)
+    assert v[0] == 1.0 and v[1] == -2.0 and np.isinf(v[2])
+    assert v[3] == 2.0 ** -133
+    assert v[4] == (2.0 - 2.0 ** -7) * 2.0 ** 127
+    assert v[5] == 0.5
+
+
+def test_e4m3_table_closed_form_values():
+    t = numerics.E4M3_TABLE
+    # OCP 8-bit FP spec, E4M3: bias 7, max normal 448 (S.1111.110), min normal 2^-6,
+    # min subnormal 2^-9, NaN only at S.1111.111, no infinities.
+    assert t[0x00] == 0.0 and t[0x80] == 0.0 and math.copysign(1, t[0x80]) == -1
+    assert t[0x01] == 2.0 ** -9 and t[0x07] == 7 * 2.0 ** -9
+    assert t[0x08] == 2.0 ** -6
+    assert t[0x38] == 1.0 and t[0x30] == 0.5 and t[0x40] == 2.0
+    assert t[0x77] == 240.0 and t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert np.isfinite(t).sum() == 254 and not np.isinf(t).any()
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0), "positive codes must be strictly increasing"
+    assert np.array_equal(t[0x80:0xFF], -t[:0x7F])
+
+
+def test_e8m0_decode():
+    s = np.array([0, 1, 127, 128, 254, 255], dtype=np.uint8)
+    v = numerics.e8m0_to_f64(s)
+    assert v[0] == 2.0 ** -127 and v[1] == 2.0 ** -126 and v[2] == 1.0 and v[3] == 2.0
+    assert v[4] == 2.0 ** 127 and np.isnan(v[5])
+
+
+def test_mxfp8_dequant_unit_and_uniform_scales():
+    rng = np.random.default_rng(0)
+    codes = rng.integers(0, 256, size=(3, 64), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                   # avoid NaN codes
+    unit = numerics.mxfp8_dequant(codes, np.full((3, 2), 127, np.uint8))
+    assert np.array_equal(unit, numerics.E4M3_TABLE[codes])
+    sc = np.array([[120, 130]] * 3, dtype=np.uint8)
+    d = numerics.mxfp8_dequant(codes, sc)
+    assert np.array_equal(d[:, :32], unit[:, :32] * 2.0 ** -7)
+    assert np.array_equal(d[:, 32:], unit[:, 32:] * 2.0 ** 3)
+
+
+def test_quantiser_round_trip_powers_of_two_exact():
+    # blocks whose elements are powers of two within 2^-9 of the block max are exact in E4M3
+    x = np.array([[2.0 ** (-(i % 9)) * (-1) ** i for i in range(32)],
+                  [0.0] * 32], dtype=np.float32)
+    q, s = synth.mxfp8_quantize(x)
+    assert s[1, 0] == 0 and not q[1].any()                 # all-zero block
+    back = numerics.mxfp8_dequant(q, s)
+    assert np.array_equal(back, x.astype(np.float64))
+
+
+def test_quantiser_error_bound():
+    # RNE to 3 mantissa bits: |x - deq| <= 2^-4 |x| on normals, <= half subnormal step otherwise;
+    # with X = floor(log2 amax) - 8 a block max scales into [256, 512), and magnitudes above 448
+    # saturate to 448 (OCP MX conversion), so there the error is |x| - 448 * 2^X.
+    x = synth.normal_f32((64, 256), seed=7)
+    q, s = synth.mxfp8_quantize(x)
+    back = numerics.mxfp8_dequant(q, s)
+    scale = numerics.e8m0_to_f64(s).repeat(32, axis=-1)
+    err = np.abs(back - x)
+    sat = np.abs(x) > 448 * scale
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, scale * 2.0 ** -10)
+    bound = np.where(sat, np.abs(x) - 448 * scale, bound)
+    assert np.all(err <= bound * (1 + 1e-12))
+    assert np.all(np.abs(back[sat]) == 448 * scale[sat])
+    # block maxima land near the top of the E4M3 range (floor(log2 amax) - 8 keeps amax < 512*2^X)
+    assert np.all(np.abs(back).reshape(64, 8, 32).max(-1) <= 448 * numerics.e8m0_to_f64(s))
+
+
+def test_bf16_rounding_of_inputs_is_rne():
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: RNE goes to the even mantissa (1.0)
+    x = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -8 + 2 ** -20], np.float32)
+    v = numerics.bf16_bits_to_f64(synth.f32_to_bf16_bits(x))
+    assert v[0] == 1.0 and v[1] == 1 + 2 ** -6 and v[2] == -1.0 and v[3] == 1 + 2 ** -7
+
+
+# ---------------------------------------------------------------------------------------------
+# GEMM formulas
+# ---------------------------------------------------------------------------------------------
+
+def test_hand_computed_2x3():
+    # A non-symmetric, non-square example worked by hand: catches transposed operands.
+    X = np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]])          # [T=2, in=3]
+    W = np.array([[1.0, 0.0, -1.0], [2.0, 1.0, 0.0]])        # [out=2, in=3]
+    dY = np.array([[1.0, -1.0], [0.5, 2.0]])                 # [T=2, out=2]
+    assert np.array_equal(linear.linear_fwd(X, W), [[-2.0, 4.0], [-2.0, 13.0]])
+    assert np.array_equal(linear.linear_dgrad(dY, W), [[-1.0, -1.0, -1.0], [4.5, 2.0, -0.5]])
+    G0 = np.array([[10.0, 0.0, 0.0], [0.0, 0.0, 1.0]])
+    # dY^T X = [[1*1+0.5*4, 1*2+0.5*5, 1*3+0.5*6], [-1*1+2*4, -1*2+2*5, -1*3+2*6]]
+    want = G0 + np.array([[3.0, 4.5, 6.0], [7.0, 8.0, 9.0]])
+    assert np.array_equal(linear.linear_wgrad_accum(G0, X, dY), want)
+
+
+@pytest.mark.parametrize("T,n_in,n_out", [(1, 1, 1), (2, 3, 5), (5, 17, 3), (3, 2, 33), (17, 5, 2)])
+def test_brute_force_tiny(T, n_in, n_out):
+    rng = np.random.default_rng(T * 100 + n_in * 10 + n_out)
+    X = synth.f32_to_bf16_bits(rng.standard_normal((T, n_in)).astype(np.float32))
+    W = synth.f32_to_bf16_bits(rng.standard_normal((n_out, n_in)).astype(np.float32))
+    dY = synth.f32_to_bf16_bits(rng.standard_normal((T, n_out)).astype(np.float32))
+    G0 = rng.standard_normal((n_out, n_in))
+    tol = 1e-12
+    np.testing.assert_allclose(linear.linear_fwd(X, W), linear.fwd_brute(X, W), rtol=tol, atol=tol)
+    np.testing.assert_allclose(linear.linear_dgrad(dY, W), linear.dgrad_brute(dY, W), rtol=tol, atol=tol)
+    np.testing.assert_allclose(linear.linear_wgrad_accum(G0, X, dY),
+                               linear.wgrad_accum_brute(G0, X, dY), rtol=tol, atol=tol)
+
+
+def test_exact_special_cases():
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((7, 5))
+    X = np.zeros((4, 5)); X[np.arange(4), [0, 2, 4, 1]] = 1.0     # one-hot rows
+    Y = linear.linear_fwd(X, W)
+    for t, i0 in enumerate([0, 2, 4, 1]):
+        assert np.array_equal(Y[t], W[:, i0])                     # a column of W
+    dY = np.zeros((3, 7)); dY[np.arange(3), [6, 0, 3]] = 1.0
+    dX = linear.linear_dgrad(dY, W)
+    for t, o0 in enumerate([6, 0, 3]):
+        assert np.array_equal(dX[t], W[o0])                       # a row of W
+    Wsq = np.eye(5)
+    X2 = rng.standard_normal((6, 5))
+    assert np.array_equal(linear.linear_fwd(X2, Wsq), X2)          # W = I
+    x1 = rng.standard_normal((1, 5)); g1 = rng.standard_normal((1, 7))
+    assert np.array_equal(linear.linear_wgrad_accum(np.zeros((7, 5)), x1, g1), np.outer(g1[0], x1[0]))
+
+
+def test_power_of_two_scaling_is_exact():
+    rng = np.random.default_rng(4)
+    X, W, dY = rng.standard_normal((9, 6)), rng.standard_normal((4, 6)), rng.standard_normal((9, 4))
+    assert np.array_equal(linear.linear_fwd(X * 8, W / 4), linear.linear_fwd(X, W) * 2)
+    assert np.array_equal(linear.linear_dgrad(dY / 2, W * 16), linear.linear_dgrad(dY, W) * 8)
+    z = np.zeros((4, 6))
+    assert np.array_equal(linear.linear_wgrad_accum(z, X * 4, dY * 4), linear.linear_wgrad_accum(z, X, dY) * 16)
+
+
+# ---------------------------------------------------------------------------------------------
+# Accumulation ([ATLAS-TP] section 4.2 fusion; [ATLAS-BUF] sections 6.4 and 6.6)
+# ---------------------------------------------------------------------------------------------
+
+def test_accumulation_linearity_and_zero_start():
+    rng = np.random.default_rng(5)
+    W = rng.standard_normal((6, 4))
+    Xs = [rng.standard_normal((8, 4)) for _ in range(3)]
+    dYs = [rng.standard_normal((8, 6)) for _ in range(3)]
+    _, _, G = linear.step(W, Xs, dYs)
+    parts = sum(dY.T @ X for X, dY in zip(Xs, dYs))
+    np.testing.assert_allclose(G, parts, rtol=1e-12, atol=1e-12)
+    # the sum of micro-batch wgrads equals one wgrad over the concatenated tokens
+    np.testing.assert_allclose(G, linear.linear_wgrad(np.vstack(Xs), np.vstack(dYs)), rtol=1e-12, atol=1e-12)
+    _, _, G1 = linear.step(W, Xs[:1], dYs[:1])
+    assert np.array_equal(G1, linear.linear_wgrad(Xs[0], dYs[0]))
+    _, _, G2 = linear.step(W, [Xs[0]] * 2, [dYs[0]] * 2)
+    assert np.array_equal(G2, 2 * G1)                                  # same data twice, bitwise
+    _, _, Gc = linear.step(W, Xs[1:], dYs[1:], main_grad0=G1)          # accumulation continues
+    np.testing.assert_allclose(Gc, G, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# TP sharding invariants ([ATLAS-TP] section 1: column then row needs one reduction per pair)
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tp", [1, 2, 4])
+def test_column_then_row_composition(tp):
+    rng = np.random.default_rng(10 + tp)
+    h, f, T = 8, 16, 5
+    W1 = rng.standard_normal((f, h))        # column-parallel: split along out (rows)
+    W2 = rng.standard_normal((h, f))        # row-parallel: split along in (columns)
+    X = rng.standard_normal((T, h))
+    dY = rng.standard_normal((T, h))
+    full_Z = linear.linear_fwd(X, W1)
+    full_Y = linear.linear_fwd(full_Z, W2)
+    c = f // tp
+    shards = [(W1[r * c:(r + 1) * c], W2[:, r * c:(r + 1) * c]) for r in range(tp)]
+    # forward: each rank's column output feeds its row shard; partial sums add to the full Y
+    partial = [linear.linear_fwd(linear.linear_fwd(X, a), b) for a, b in shards]
+    np.testing.assert_allclose(sum(partial), full_Y, rtol=1e-12, atol=1e-12)
+    # backward (identity activation): row dgrad is the full dZ restricted to the rank's slice
+    full_dZ = linear.linear_dgrad(dY, W2)
+    for r, (a, b) in enumerate(shards):
+        np.testing.assert_allclose(linear.linear_dgrad(dY, b), full_dZ[:, r * c:(r + 1) * c], rtol=1e-12, atol=1e-12)
+    # column dgrad partials summed over ranks give the unsharded dX (the all-reduce of f)
+    dX_parts = [linear.linear_dgrad(full_dZ[:, r * c:(r + 1) * c], a) for r, (a, _) in enumerate(shards)]
+    np.testing.assert_allclose(sum(dX_parts), linear.linear_dgrad(full_dZ, W1), rtol=1e-12, atol=1e-12)
+    # each shard's wgrad is the matching slice of the unsharded wgrad
+    G1 = linear.linear_wgrad(X, full_dZ)
+    G2 = linear.linear_wgrad(full_Z, dY)
+    for r, (a, b) in enumerate(shards):
+        zr = linear.linear_fwd(X, a)
+        np.testing.assert_allclose(linear.linear_wgrad(X, full_dZ[:, r * c:(r + 1) * c]), G1[r * c:(r + 1) * c], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(linear.linear_wgrad(zr, dY), G2[:, r * c:(r + 1) * c], rtol=1e-12, atol=1e-12)
+
+
+def test_tp1_shard_is_the_unsharded_layer():
+    rng = np.random.default_rng(20)
+    W = rng.standard_normal((6, 4)); X = rng.standard_normal((3, 4)); dY = rng.standard_normal((3, 6))
+    shard = W[0:6, 0:4]                                   # the only shard at TP=1
+    assert np.array_equal(linear.linear_fwd(X, shard), linear.linear_fwd(X, W))
+    assert np.array_equal(linear.linear_dgrad(dY, shard), linear.linear_dgrad(dY, W))
+
+
+# ---------------------------------------------------------------------------------------------
+# Shapes ([MEGA-SRC] section 1)
+# ---------------------------------------------------------------------------------------------
+
+def test_llama_1b_param_ledger():
+    cfg = shapes.LLAMA_1B
+    assert shapes.per_layer_params(**cfg) == 60_821_504
+    assert cfg["L"] * shapes.per_layer_params(**cfg) == 973_144_064
+    assert cfg["v"] * cfg["h"] == 262_668_288
+    assert shapes.total_params(**cfg) == 1_498_482_688
+    per_card = shapes.total_params(**cfg) / (2 * 2)       # PP=2 stages, TP=2 halves
+    assert round(per_card / 1e6, 1) == 374.6
+    assert round(per_card * (2 + 4 + 12 / 2) / 1e9, 2) == 4.50   # 12 B per TP-local param
+    assert round(per_card * 12 / 2 ** 30, 2) == 4.19
+
+
+def test_tp2_shards_add_up_to_the_layer():
+    cfg = shapes.LLAMA_1B
+    sh = shapes.tp_shard_shapes(**cfg, tp=2)
+    assert sh == {"linear_qkv": (1536, 2048), "linear_proj": (2048, 1024),
+                  "linear_fc1": (8192, 2048), "linear_fc2": (2048, 4096)}
+    per_rank = sum(o * i for o, i in sh.values())
+    assert per_rank == 30_408_704
+    assert 2 * per_rank + 2 * cfg["h"] == shapes.per_layer_params(**cfg)
+
+
+# ---------------------------------------------------------------------------------------------
+# Layout ([ATLAS-BUF] sections 4-5, [MEGA-SRC] section 6.3 toy)
+# ---------------------------------------------------------------------------------------------
+
+def test_toy_layout_matches_printed_output():
+    g = json.load(open(os.path.join(GOLDEN, "toy_layout.json")))
+    names = [n for n, _ in g["definition_order"]]
+    lay = layout.build_layout([k for _, k in g["definition_order"]], param_align=g["param_align"],
+                              bucket_size=None, dp=g["dp"], divisor=g["divisor"])
+    exp = g["expected"]
+    assert lay.numel == exp["numel"]
+    assert lay.buckets[0][1] - lay.buckets[0][2] == exp["pad"]
+    for i, n in enumerate(names):
+        assert [lay.start[i], lay.end[i]] == exp["ranges"][n]
+    shards = layout.shard_ranges(0, lay.numel, g["dp"])
+    assert shards[0][1] == exp["shard_boundary"]
+    wl = names.index("WL")
+    lo, hi = lay.start[wl], lay.end[wl]
+    assert [lo - lo, min(hi, shards[0][1]) - 1 - lo] == exp["WL_elements_on_rank0"]
+    assert [shards[1][0] - lo, hi - 1 - lo] == exp["WL_elements_on_rank1"]
+
+
+def test_7b_bucket_ledger():
+    # [ATLAS-BUF] section 8: P' = 1.875e9 elements per rank, dp=64, bucket_size = max(40M, 64M)
+    # = 64M elements -> about 29 full buckets + 1 tail, padding <= 2^16 - 1 per bucket (high
+    # bus-bandwidth padding), about 1.9M padding elements in total.  Parameters of 1e6 elements
+    # (a multiple of 64, so no start padding) stand in for the fine-grained parameter list.
+    dp = 64
+    bs = layout.default_bucket_size(dp)
+    assert bs == 64_000_000
+    lay = layout.build_layout([1_000_000] * 1875, param_align=64, bucket_size=bs, dp=dp,
+                              divisor=layout.bucket_divisor(dp, high_busbw=True))
+    full = [b for b in lay.buckets if b[2] >= bs]
+    assert len(full) == 29 and len(lay.buckets) == 30
+    pads = [b[1] - b[2] for b in lay.buckets]
+    assert max(pads) <= 2 ** 16 - 1 and all(b[1] % dp == 0 for b in lay.buckets)
+    assert sum(pads[:29]) <= 29 * (2 ** 16 - 1)
+    assert round(lay.numel * 4 / 1e9, 1) == 7.5                       # grad_data fp32 7.5 GB
+    assert round(lay.numel * 2 / 1e9, 2) == 3.75                      # param_data bf16 3.75 GB
+    assert round(bs * 4 / 1e6) == 256                                 # 256 MB per bucket RS
+
+
+def test_divisor_and_default_bucket_size():
+    assert layout.bucket_divisor(1) == 128 and layout.bucket_divisor(2) == 128
+    assert layout.bucket_divisor(3) == 384 and layout.bucket_divisor(64) == 128
+    assert layout.bucket_divisor(64, high_busbw=True) == 65536
+    assert layout.bucket_divisor(3, high_busbw=True) == 3 * 65536
+    assert layout.default_bucket_size(1) == 40_000_000
+    assert layout.default_bucket_size(64) == 64_000_000
+
+
+def test_config_layouts():
+    # C2, one TP=2 rank's MLP: fc1 [8192,2048] then fc2 [2048,4096] in definition order.
+    lay = layout.build_layout([8192 * 2048, 2048 * 4096], bucket_size=layout.default_bucket_size(1))
+    assert (lay.start, lay.end) == ([8_388_608, 0], [25_165_824, 8_388_608])
+    assert lay.numel == 25_165_824 and len(lay.buckets) == 1
+    # C4, 7B-class layer shards at dp=1 (qkv, proj, fc1, fc2): bucket 0 closes after fc1.
+    n = [6144 * 4096, 4096 * 2048, 11008 * 4096, 4096 * 5504]
+    lay = layout.build_layout(n, bucket_size=layout.default_bucket_size(1))
+    assert lay.start == [76_021_760, 67_633_152, 22_544_384, 0]
+    assert lay.bucket_id == [1, 1, 0, 0]
+    assert lay.buckets == [(0, 67_633_152, 67_633_152), (67_633_152, 33_554_432, 33_554_432)]
+    # C1: a single [512,256] weight at offset 0 of a 131072-element buffer (a multiple of 64)
+    lay = layout.build_layout([512 * 256], bucket_size=None)
+    assert (lay.start, lay.numel) == ([0], 131_072) and lay.numel % 64 == 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_layout_properties_random(seed):
+    rng = np.random.default_rng(seed)
+    numels = [int(x) for x in rng.integers(1, 5000, size=int(rng.integers(1, 40)))]
+    dp = int(rng.choice([1, 2, 3, 8]))
+    bs = int(rng.integers(100, 20000))
+    div = layout.bucket_divisor(dp)
+    lay = layout.build_layout(numels, param_align=64, bucket_size=bs, dp=dp, divisor=div)
+    n = len(numels)
+    for i in range(n):
+        assert lay.start[i] % 64 == 0 and lay.end[i] - lay.start[i] == numels[i]
+    for i in range(n - 1):          # reverse order: a later-defined param sits at a lower offset
+        assert lay.end[i + 1] <= lay.start[i]
+    prev = 0
+    for b, (off, num, unp) in enumerate(lay.buckets):
+        assert off == prev and num % div == 0 and num - unp < div and unp <= num
+        members = [i for i in range(n) if lay.bucket_id[i] == b]
+        assert members, "no empty buckets"
+        last = min(members)          # the bucket's last-placed param (lowest definition index)
+        assert lay.end[last] - off == unp
+        if b < len(lay.buckets) - 1:
+            assert unp >= bs          # a bucket closes only once it reaches bucket_size ...
+            before = [lay.end[i] for i in members if i != last]
+            assert all(e - off < bs for e in before)   # ... and not earlier
+        prev = off + num
+    assert lay.numel == prev
