@@ -1,0 +1,240 @@
+"""Throughput of one TP rank's linear step on one MI355X, against the MFMA roofline.
+
+A step is one pass of the whole hot path over one batch of synthetic input: zero the fp32
+grad_data once, then for every micro-batch run the forward GEMM of each weight shard, and in
+backward order its dgrad and its fused fp32 wgrad-accumulate into the main_grad view.  Inputs
+are resident in HBM before timing starts.  The value is algorithmic TFLOP/s (2*T*in*out per
+GEMM) of the timed steps; each kernel launch is also bracketed by HIP events on the launch
+stream to give the per-kernel roofline figures.
+
+    python bench.py [--steps K] [--warmup W] [--config c2|c1|c3|c4|c5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s fwd+dgrad+wgrad per TP-sharded linear; % of MI355X MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}      # MI355X published dense MFMA peaks
+HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="c2")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-kernel-events", action="store_true",
+                   help="time whole steps only (no per-launch events)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's shard only: run it with --gpus 1 (multi-GPU collectives "
+              "are not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sharded_linear_amd as sl
+    from synth import configs
+
+    w = configs.WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def dev_u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---- set-up: layout, buffers, weights, all micro-batches resident in HBM ----------------
+    t0 = time.time()
+    buf = sl.ParamAndGradBuffer(w.params, dev)
+    names = list(w.step_params)
+    wq = {}
+    for n in names:
+        wt = configs.weight(w, n)
+        if w.mxfp8:
+            wq[n] = (dev_u8(wt[0]), dev_u8(wt[1]))
+        else:
+            buf.param(n).copy_(dev_bf16(wt))
+    xs, dys = [], []
+    for k in range(w.microbatches):
+        xk, dyk = {}, {}
+        for n in names:
+            xv = configs.x(w, n, k)
+            xk[n] = (dev_u8(xv[0]), dev_u8(xv[1])) if w.mxfp8 else dev_bf16(xv)
+            dyk[n] = dev_bf16(configs.dy(w, n, k))
+        xs.append(xk)
+        dys.append(dyk)
+    T = w.tokens
+    ys = {n: torch.empty((T, w.params[n][0]), dtype=torch.bfloat16, device=dev) for n in names}
+    dxs = {n: torch.empty((T, w.params[n][1]), dtype=torch.bfloat16, device=dev) for n in names}
+    wss = {}
+    for n in names:
+        o, i = w.params[n]
+        nb = sl.sl_wgrad_workspace_bytes(T, i, o)
+        wss[n] = torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev) if nb else None
+    torch.cuda.synchronize()
+    log(f"set-up {time.time() - t0:.1f}s: {w.title}; grad_data {buf.numel} elements")
+
+    # ---- one step --------------------------------------------------------------------------
+    stream = torch.cuda.current_stream(dev)
+    records = []        # (kind, flops, start_event, end_event) of the timed steps
+
+    def launch(kind, flops, fn, *a, timed):
+        if timed:
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            fn(*a)
+            e.record(stream)
+            records.append((kind, flops, s, e))
+        else:
+            fn(*a)
+
+    def step(timed=False):
+        launch("zero", 0, sl.sl_grad_buffer_zero, buf.grad_data, timed=timed)
+        for k in range(w.microbatches):
+            for n in names:
+                o, i = w.params[n]
+                f = 2 * T * i * o
+                if w.mxfp8:
+                    launch("fwd", f, sl.sl_linear_fwd_mxfp8, *xs[k][n], *wq[n], ys[n], timed=timed)
+                else:
+                    launch("fwd", f, sl.sl_linear_fwd, xs[k][n], buf.param(n), ys[n], timed=timed)
+            for n in reversed(names):
+                o, i = w.params[n]
+                f = 2 * T * i * o
+                if w.mxfp8:
+                    launch("dgrad", f, sl.sl_linear_dgrad_mxfp8w, dys[k][n], *wq[n], dxs[n], timed=timed)
+                    launch("wgrad", f, sl.sl_linear_wgrad_accum_mxfp8x, *xs[k][n], dys[k][n],
+                           buf.main_grad(n), wss[n], timed=timed)
+                else:
+                    launch("dgrad", f, sl.sl_linear_dgrad, dys[k][n], buf.param(n), dxs[n], timed=timed)
+                    launch("wgrad", f, sl.sl_linear_wgrad_accum, xs[k][n], dys[k][n], buf.main_grad(n),
+                           wss[n], timed=timed)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step(timed=not args.no_kernel_events)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = w.flops_per_step()
+    tflops = flops / (ms * 1e-3) / 1e12
+    dtype = "bf16"        # the MXFP8 operands are dequantised exactly to bf16 and run bf16 MFMA
+    peak = PEAK_TFLOPS[dtype]
+
+    # ---- per-kernel figures from the events -----------------------------------------------
+    kinds = {}
+    for kind, f, s, e in records:
+        d = kinds.setdefault(kind, {"launches": 0, "ms": 0.0, "flops": 0})
+        d["launches"] += 1
+        d["ms"] += s.elapsed_time(e)
+        d["flops"] += f
+    kernels = {}
+    for kind, d in kinds.items():
+        avg_us = d["ms"] / d["launches"] * 1e3
+        kernels[kind] = {"launches_per_step": d["launches"] // args.steps, "avg_us": round(avg_us, 2),
+                         "share_of_step": round(d["ms"] / args.steps / ms, 4)}
+        if d["flops"]:
+            kernels[kind]["tflops"] = round(d["flops"] / (d["ms"] * 1e-3) / 1e12, 1)
+    roofline = None
+    gemm = {k: v for k, v in kinds.items() if v["flops"]}
+    if gemm:
+        dom = max(gemm, key=lambda k: gemm[k]["ms"])
+        d = gemm[dom]
+        ach = d["flops"] / (d["ms"] * 1e-3) / 1e12
+        roofline = {"kernel": f"linear_{dom}", "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                    "per_launch_flops": d["flops"] // d["launches"], "avg_launch_us": round(d["ms"] / d["launches"] * 1e3, 2)}
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w)
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) activations/grads, N(0,0.02^2) weights, bf16 RNE)",
+        "config": {"workload": w.title, "key": w.key, "tokens": T, "microbatches": w.microbatches,
+                   "shards_out_in": {n: list(w.params[n]) for n in names},
+                   "flops_per_step": flops, "step": "zero grad_data; per micro-batch: fwd of each "
+                   "shard, then dgrad + fused fp32 wgrad-accumulate in backward order"},
+        "frac_of_peak": round(tflops / peak, 4),
+        "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w):
+    """The oracle (numpy float64, BLAS dgemm) timed on the host over whole micro-batches of the
+    same workload until about 10 s have passed."""
+    import numpy as np
+    from oracle import linear as ol
+    from synth import configs
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=0)
+    except Exception:                       # threadpoolctl missing: report the affinity mask
+        threads = 0
+    cores = threads or len(os.sched_getaffinity(0))
+    if w.mxfp8:
+        log("cpu baseline: MXFP8 workload, oracle dequantises per block first")
+    names = list(w.step_params)
+    weights = {n: configs.weight(w, n) for n in names}
+    done_flops, elapsed, mbs = 0, 0.0, 0
+    for k in range(w.microbatches):
+        xk = {n: configs.x(w, n, k) for n in names}
+        dyk = {n: configs.dy(w, n, k) for n in names}
+        t = time.perf_counter()
+        for n in names:
+            G = np.zeros(w.params[n])
+            if w.mxfp8:
+                ol.linear_fwd_mxfp8(*xk[n], *weights[n])
+                ol.linear_dgrad_mxfp8w(dyk[n], *weights[n])
+                ol.linear_wgrad_accum_mxfp8x(G, *xk[n], dyk[n])
+            else:
+                ol.step(weights[n], [xk[n]], [dyk[n]], main_grad0=G)
+        elapsed += time.perf_counter() - t
+        done_flops += sum(6 * w.tokens * o * i for o, i in (w.params[n] for n in names))
+        mbs += 1
+        log(f"cpu baseline: micro-batch {k} done, {elapsed:.1f}s")
+        if elapsed > 10.0:
+            break
+    return {"value": round(done_flops / elapsed / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{mbs} of {w.microbatches} micro-batches of the same workload (fwd, dgrad, "
+                      f"wgrad-accumulate of every shard), numpy float64, {elapsed:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,139 @@
+/*
+ * sharded_linear.h -- C ABI of one tensor-parallel rank's linear step on gfx950 (MI355X).
+ *
+ * The step (llm-infra-atlas, "01 · ColumnParallelLinear / RowParallelLinear and the core
+ * autograd", section 4): forward Y = X.W^T, input gradient dX = dY.W, and the weight gradient
+ * fused into gradient accumulation, main_grad += dY^T.X in fp32, where main_grad is a view of a
+ * flat grad_data buffer and W a view of a matching param_data buffer (llm-infra-atlas,
+ * "05 · grad/param buffer", sections 4-5).  Collectives are not part of this library.
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are row-major and dense: the leading dimension is the last extent.
+ *       X, dX : [T, in]     W : [out, in]     Y, dY : [T, out]     main_grad : [out, in]
+ *     T = tokens (sequence x micro-batch rows flattened), in/out = the shard's features.
+ *   - bf16 tensors are passed as raw 16-bit storage; main_grad and grad_data are fp32.
+ *   - Device pointers must be 16-byte aligned; in and out must be multiples of 8 (32 for the
+ *     MXFP8 entry points); T may be any value >= 0.  A zero extent is a no-op.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null stream) and
+ *     performs no synchronisation, no allocation and no free.  The caller owns all memory.
+ *   - Arguments are validated on the host before any HIP call; on error nothing is launched.
+ *   - Return value: SL_OK (0) or a negative SL_E* status; sl_status_str() names it.
+ *   - Results of the GEMMs are deterministic: the same inputs give the same bits.
+ */
+#ifndef SHARDED_LINEAR_H
+#define SHARDED_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SL_OK = 0,
+  SL_EINVAL = -1,      /* null pointer with a nonzero extent, negative extent, bad option      */
+  SL_EALIGN = -2,      /* device pointer not 16-byte aligned                                   */
+  SL_ESHAPE = -3,      /* in/out not a multiple of 8 (32 for MXFP8), or an extent >= 2^31       */
+  SL_EWORKSPACE = -4,  /* workspace missing or smaller than sl_wgrad_workspace_bytes()          */
+  SL_EHIP = -5,        /* the HIP runtime reported an error at launch                          */
+  SL_ECAPACITY = -6    /* an output array given to sl_layout_build is too small                */
+};
+
+/* Name of a status code (static storage). */
+const char* sl_status_str(int status);
+
+/* ---------------------------------------------------------------------------------------------
+ * Buffer layout (host only; llm-infra-atlas "05 · grad/param buffer", sections 4.1-4.3 and 5).
+ *
+ * Places n parameters, numel[] given in model definition order, into one flat buffer:
+ *   - in reverse definition order (backprop order), so offset 0 holds the last parameter;
+ *   - each parameter start rounded up to a multiple of param_align elements (64 under the
+ *     distributed optimizer; the page notes the unit is elements, not bytes);
+ *   - a bucket is closed right after the parameter whose end makes (end - bucket_start) reach
+ *     bucket_size elements; bucket_size <= 0 puts everything in one bucket;
+ *   - each bucket end is rounded up to a multiple of `divisor` (lcm(dp,128), or
+ *     lcm(dp,128,65536) with the high-bus-bandwidth option, see sl_bucket_divisor), and the next
+ *     bucket starts there.
+ * Outputs (caller-owned host arrays): start/end/bucket_id per parameter (definition order);
+ * per bucket: offset, padded numel and unpadded numel (param end - bucket start), up to
+ * bucket_cap entries; *n_buckets and *total_numel.  If bucket_cap is too small the call
+ * returns SL_ECAPACITY and sets *n_buckets to the number needed.  A zero-size parameter is
+ * allowed; n = 0 gives total_numel 0 and no buckets.
+ * ------------------------------------------------------------------------------------------- */
+int sl_layout_build(int32_t n, const int64_t* numel, int64_t param_align, int64_t bucket_size,
+                    int64_t divisor, int64_t* start, int64_t* end, int32_t* bucket_id,
+                    int32_t bucket_cap, int64_t* bucket_offset, int64_t* bucket_numel,
+                    int64_t* bucket_numel_unpadded, int32_t* n_buckets, int64_t* total_numel);
+
+/* Default bucket size in elements, max(40,000,000, 1,000,000 * dp) (same page, section 4.3). */
+int64_t sl_default_bucket_size(int64_t dp);
+
+/* Bucket-end divisor lcm(dp, 128), or lcm(dp, 128, 65536) when high_busbw != 0 (section 4.2).
+ * Returns 0 for dp <= 0. */
+int64_t sl_bucket_divisor(int64_t dp, int32_t high_busbw);
+
+/* ---------------------------------------------------------------------------------------------
+ * Gradient-buffer zeroing (same page, section 6.6: grad_data is zeroed once per iteration and
+ * never freed).  Writes 0.0f to grad_data[0, numel).  A fill kernel, so it is safe to record in
+ * a captured HIP graph.  Also used to prepare a wgrad workspace before its first use.
+ * ------------------------------------------------------------------------------------------- */
+int sl_grad_buffer_zero(void* stream, float* grad_data, int64_t numel);
+
+/* ---------------------------------------------------------------------------------------------
+ * Forward GEMM: Y[T,out] = X[T,in] . W[out,in]^T, bf16 inputs, fp32 accumulation, one
+ * round-to-nearest-even to bf16 (atlas page "01", section 4.1).  For a row-parallel weight Y is
+ * the partial sum that the following all-reduce would add up.
+ * ------------------------------------------------------------------------------------------- */
+int sl_linear_fwd(void* stream, const void* X, const void* W, void* Y,
+                  int64_t T, int64_t in, int64_t out);
+
+/* ---------------------------------------------------------------------------------------------
+ * Input-gradient GEMM: dX[T,in] = dY[T,out] . W[out,in], bf16 in/out, fp32 accumulation
+ * (atlas page "01", section 4.2, the dgrad).
+ * ------------------------------------------------------------------------------------------- */
+int sl_linear_dgrad(void* stream, const void* dY, const void* W, void* dX,
+                    int64_t T, int64_t in, int64_t out);
+
+/* ---------------------------------------------------------------------------------------------
+ * Weight gradient fused into accumulation: main_grad[out,in] += dY[T,out]^T . X[T,in] in fp32
+ * (atlas page "01", section 4.2, gradient_accumulation_fusion).  The micro-batch gradient is
+ * never rounded and never stored on its own; main_grad is read and written only inside its
+ * [out, in] extent, so neighbouring views and padding of grad_data are untouched.
+ *
+ * workspace: device memory of at least sl_wgrad_workspace_bytes(T, in, out) bytes (may be 0, in
+ * which case workspace may be NULL).  It holds split-K partial tiles and per-tile arrival
+ * counters.  The counters must be zero before the workspace is first used (sl_grad_buffer_zero
+ * on the whole workspace, or zero-filled allocation); every call leaves them zero again.  Calls
+ * that may run concurrently must use distinct workspaces.
+ * ------------------------------------------------------------------------------------------- */
+size_t sl_wgrad_workspace_bytes(int64_t T, int64_t in, int64_t out);
+int sl_linear_wgrad_accum(void* stream, const void* X, const void* dY, float* main_grad,
+                          int64_t T, int64_t in, int64_t out,
+                          void* workspace, size_t workspace_bytes);
+
+/* ---------------------------------------------------------------------------------------------
+ * MXFP8 operand variants (NVIDIA Megatron-Core guide "Generalized Tensor Parallelism",
+ * section 1.3: E4M3 elements with one E8M0 scale per 32 elements).  A quantised matrix M[r, c]
+ * is passed as codes Mq[r, c] (uint8, E4M3FN) and scales Ms[r, c/32] (uint8, E8M0), and stands
+ * for deq(q, s) = E4M3(q) * 2^(s - 127).  Blocks run along `in` for both X and W.
+ *   fwd:   Y  = deq(Xq).deq(Wq)^T           (bf16 out)
+ *   dgrad: dX = dY.deq(Wq)                  (dY, dX bf16)
+ *   wgrad: main_grad += dY^T.deq(Xq)        (dY bf16, main_grad fp32)
+ * Every dequantised element must be representable in bf16 (an E4M3 value times a power of two
+ * whose result is a normal bf16); it then enters the GEMMs exactly.  in must be a multiple of
+ * 32.  The wgrad workspace contract is the one of sl_linear_wgrad_accum.
+ * ------------------------------------------------------------------------------------------- */
+int sl_linear_fwd_mxfp8(void* stream, const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
+                        const uint8_t* Ws, void* Y, int64_t T, int64_t in, int64_t out);
+int sl_linear_dgrad_mxfp8w(void* stream, const void* dY, const uint8_t* Wq, const uint8_t* Ws,
+                           void* dX, int64_t T, int64_t in, int64_t out);
+int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, const uint8_t* Xs,
+                                 const void* dY, float* main_grad, int64_t T, int64_t in,
+                                 int64_t out, void* workspace, size_t workspace_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHARDED_LINEAR_H */

@@ -1,0 +1,603 @@
+// GEMM kernels of one tensor-parallel rank's linear step, written for gfx950 (CDNA4, MI355X).
+//
+// The three products of llm-infra-atlas, "01 · ColumnParallelLinear / RowParallelLinear and the
+// core autograd", sections 4.1-4.2:
+//   fwd    Y[T,out]        = X[T,in] . W[out,in]^T        M=T   N=out K=in
+//   dgrad  dX[T,in]        = dY[T,out] . W[out,in]        M=T   N=in  K=out
+//   wgrad  main_grad[out,in] += dY[T,out]^T . X[T,in]     M=out N=in  K=T   (fp32, in place)
+// All three are one kernel template: C[m][n] (+)= sum_k A(m,k) B(n,k).  An operand is stored
+// either with k contiguous ("K-major": X and W in fwd, dY in dgrad) or with m/n contiguous
+// ("MN-major": W in dgrad, dY and X in wgrad).  Both kinds are staged through LDS in one
+// layout -- rows of 64 k values, 16-byte chunks XOR-swizzled against bank conflicts -- so the
+// MFMA loop is shared; MN-major tiles are transposed in registers (8x8 blocks of bf16) on their
+// way from HBM into LDS.
+//
+// Matrix cores: v_mfma_f32_32x32x16_bf16.  Lane l supplies row (l % 32) of its A block and
+// column (l % 32) of its B block with eight consecutive k values (k offset 8*(l/32)); the
+// 32x32 fp32 result leaves lane l holding column l % 32, rows 8*(r/4) + 4*(l/32) + r%4 for
+// r = 0..15.
+//
+// MXFP8 operands (NVIDIA Megatron-Core guide "Generalized Tensor Parallelism", section 1.3:
+// E4M3 data, one E8M0 scale per 32 elements) are dequantised exactly to bf16 as they are moved
+// into LDS, then take the same MFMA path.
+//
+// Split-K for the weight gradient is deterministic: every split writes its fp32 partial tile
+// to the workspace and bumps the tile's counter; the split that arrives last adds all partials
+// in split order and performs the single read-modify-write of main_grad, then re-arms the
+// counter.  No block ever waits on another, so every launch drains.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sharded_linear.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBK = 64;           // k extent of one LDS stage
+constexpr int kCH = kBK / 8;      // 16-byte chunks per LDS row
+constexpr int kXCD = 8;           // accelerator complex dies; workgroups are dealt round-robin
+
+enum class Elem { BF16, MXFP8 };
+enum class Epi { StoreBF16, AccumF32 };
+
+struct Operand {
+  const void* p;        // bf16 storage, or E4M3 codes for MXFP8
+  const uint8_t* s;     // E8M0 scales (MXFP8 only), row-major [rows of storage][ld / 32]
+  int64_t ld;           // elements between consecutive storage rows
+  int rows;             // extent of the free (m or n) index
+};
+
+struct Args {
+  Operand a, b;
+  void* c;
+  int64_t ldc;
+  int M, N, K;
+  int tiles_m, tiles_n;
+  int splits, kt_per_split;
+  float* ws;            // split-K partial tiles
+  unsigned* cnt;        // split-K arrival counters, one per output tile
+};
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// E4M3FN code times 2^(s - 127) as bf16 bits.  Value = sig * 2^(max(e,1) - 10) with
+// sig = 8 + m for normals (e > 0) and sig = m for subnormals; exact whenever the result is a
+// normal bf16 (the caller's contract); NaN codes or the NaN scale give a quiet NaN.
+__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t code, uint32_t s) {
+  const uint32_t sign = (code & 0x80u) << 8;
+  const uint32_t e = (code >> 3) & 0xFu, m = code & 0x7u;
+  if ((code & 0x7Fu) == 0x7Fu || s == 0xFFu) return sign | 0x7FC0u;
+  if ((code & 0x7Fu) == 0) return sign;
+  int exp;
+  uint32_t mant;
+  if (e) {
+    exp = int(e) + int(s) - 7;
+    mant = m << 4;
+  } else {
+    const int p = 31 - __builtin_clz(m);            // leading bit of the subnormal field
+    exp = p + int(s) - 9;
+    mant = ((m << (3 - p)) & 0x7u) << 4;
+  }
+  if (exp <= 0) return sign;                        // outside the contract: flush
+  if (exp >= 255) return sign | 0x7F80u;
+  return sign | (uint32_t(exp) << 7) | mant;
+}
+
+// Eight E4M3 codes (one 8-byte chunk) with their block scale -> eight bf16 in a 16-byte chunk.
+__device__ __forceinline__ uint4 dequant8(uint2 q, uint32_t s) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t src = i < 2 ? q.x : q.y;
+    const int sh = (i & 1) * 16;
+    w[i] = e4m3_to_bf16((src >> sh) & 0xFFu, s) | (e4m3_to_bf16((src >> (sh + 8)) & 0xFFu, s) << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Element loader: the 8 consecutive elements of storage row `srow` starting at column `col`
+// (a multiple of 8), as a 16-byte chunk of bf16.
+template <Elem E>
+struct Chunk;
+
+template <>
+struct Chunk<Elem::BF16> {
+  uint4 v;
+  __device__ __forceinline__ void load(const Operand& op, int64_t srow, int64_t col) {
+    v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(op.p) + srow * op.ld + col);
+  }
+  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ uint4 get() const { return v; }
+};
+
+template <>
+struct Chunk<Elem::MXFP8> {
+  uint2 q;
+  uint32_t s;
+  __device__ __forceinline__ void load(const Operand& op, int64_t srow, int64_t col) {
+    q = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(op.p) + srow * op.ld + col);
+    s = op.s[srow * (op.ld / 32) + col / 32];
+  }
+  __device__ __forceinline__ void zero() { q = make_uint2(0, 0); s = 127; }
+  __device__ __forceinline__ uint4 get() const { return dequant8(q, s); }
+};
+
+// K-major operand tile: R rows (free index) x kBK k; storage row = free index, k contiguous.
+template <int R, int NT, Elem E>
+struct KMajTile {
+  static constexpr int kPasses = R * kCH / NT;
+  static_assert(kPasses * NT == R * kCH, "tile/thread mismatch");
+  Chunk<E> ch[kPasses];
+
+  __device__ __forceinline__ void load(const Operand& op, int row0, int k0, int K, int tid) {
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int r = p * (NT / kCH) + tid / kCH, c = tid % kCH;
+      const int gr = row0 + r, k = k0 + c * 8;
+      if (gr < op.rows && k < K) ch[p].load(op, gr, k); else ch[p].zero();
+    }
+  }
+  __device__ __forceinline__ void store(uint4* lds, int tid) const {
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int r = p * (NT / kCH) + tid / kCH, c = tid % kCH;
+      lds[r * kCH + (c ^ swz(r))] = ch[p].get();
+    }
+  }
+};
+
+// MN-major operand tile: storage row = k, free index contiguous.  Each thread moves blocks of
+// KB k rows x 8 consecutive free indices (KB = 8, or 4 when the tile has too few 8x8 blocks for
+// one per thread) and transposes them so that LDS again holds rows of consecutive k.
+template <int R, int NT, Elem E>
+struct MNMajTile {
+  static constexpr int KB = (R / 8) * (kBK / 8) >= NT ? 8 : 4;
+  static constexpr int kBlocks = (R / 8) * (kBK / KB);
+  static constexpr int kPer = kBlocks / NT;
+  static_assert(kPer >= 1 && kPer * NT == kBlocks, "tile/thread mismatch");
+  Chunk<E> ch[kPer][KB];
+
+  __device__ __forceinline__ void load(const Operand& op, int row0, int k0, int K, int tid) {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int q = p * NT + tid, rb = q % (R / 8), kb = q / (R / 8);
+      const int gr = row0 + rb * 8;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const int k = k0 + kb * KB + j;
+        if (gr < op.rows && k < K) ch[p][j].load(op, k, gr); else ch[p][j].zero();
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint4* lds, int tid) const {
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      const int q = p * NT + tid, rb = q % (R / 8), kb = q / (R / 8);
+      uint32_t in[KB][4];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const uint4 v = ch[p][j].get();
+        in[j][0] = v.x; in[j][1] = v.y; in[j][2] = v.z; in[j][3] = v.w;
+      }
+      // in[j] holds free indices 8rb..8rb+7 at k = KB*kb + j (two bf16 per word, even index low)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t o[KB / 2];
+#pragma unroll
+        for (int w = 0; w < KB / 2; ++w) {
+          const uint32_t lo = in[2 * w][i >> 1], hi = in[2 * w + 1][i >> 1];
+          o[w] = (i & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+        }
+        const int r = rb * 8 + i;
+        if constexpr (KB == 8) {
+          lds[r * kCH + (kb ^ swz(r))] = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+          uint2* l2 = reinterpret_cast<uint2*>(lds);
+          l2[(r * kCH + ((kb >> 1) ^ swz(r))) * 2 + (kb & 1)] = make_uint2(o[0], o[1]);
+        }
+      }
+    }
+  }
+};
+
+template <bool KMAJ, int R, int NT, Elem E>
+struct TileSel { using T = KMajTile<R, NT, E>; };
+template <int R, int NT, Elem E>
+struct TileSel<false, R, NT, E> { using T = MNMajTile<R, NT, E>; };
+
+// Deal workgroups so that each XCD works on a contiguous stretch of the tile order (tiles
+// that share operand panels then share that XCD's L2).  Hardware hands block b to XCD b % 8.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int per = n / kXCD, rem = n % kXCD, x = b % kXCD;
+  return x * per + (x < rem ? x : rem) + b / kXCD;
+}
+
+template <int BM, int BN, int WGM, int WGN, bool A_KMAJ, bool B_KMAJ, Elem EA, Elem EB, Epi EPI>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+gemm_kernel(Args args) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int WM = BM / WGM, WN = BN / WGN;        // wave tile
+  constexpr int TM = WM / 32, TN = WN / 32;          // 32x32 MFMA blocks per wave
+  using TileA = typename TileSel<A_KMAJ, BM, NT, EA>::T;
+  using TileB = typename TileSel<B_KMAJ, BN, NT, EB>::T;
+
+  __shared__ uint4 lds_a[2][BM * kCH];
+  __shared__ uint4 lds_b[2][BN * kCH];
+  __shared__ int last_flag;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  // tile coordinates: XCD-aware dealing, then groups of 8 tile rows walked column-major
+  const int ntiles = args.tiles_m * args.tiles_n;
+  const int t = xcd_remap(blockIdx.x, ntiles);
+  const int group = t / (8 * args.tiles_n);
+  const int first_m = group * 8;
+  const int gsz = min(args.tiles_m - first_m, 8);
+  const int tm = first_m + (t % (8 * args.tiles_n)) % gsz;
+  const int tn = (t % (8 * args.tiles_n)) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int split = blockIdx.z;
+  const int nkt = (args.K + kBK - 1) / kBK;
+  const int kt_begin = split * args.kt_per_split;
+  const int kt_end = min(nkt, kt_begin + args.kt_per_split);
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  TileA ta;
+  TileB tb;
+  if (kt_begin < kt_end) {
+    ta.load(args.a, m0, kt_begin * kBK, args.K, tid);
+    tb.load(args.b, n0, kt_begin * kBK, args.K, tid);
+    ta.store(lds_a[0], tid);
+    tb.store(lds_b[0], tid);
+  }
+  __syncthreads();
+
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const int cur = (kt - kt_begin) & 1;
+    const bool more = kt + 1 < kt_end;
+    if (more) {
+      ta.load(args.a, m0, (kt + 1) * kBK, args.K, tid);
+      tb.load(args.b, n0, (kt + 1) * kBK, args.K, tid);
+    }
+    const uint4* la = lds_a[cur];
+    const uint4* lb = lds_b[cur];
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      bf16x8 fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WM + i * 32 + (lane & 31);
+        const uint4 v = la[r * kCH + (c ^ swz(r))];
+        fa[i] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * WN + j * 32 + (lane & 31);
+        const uint4 v = lb[r * kCH + (c ^ swz(r))];
+        fb[j] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      ta.store(lds_a[cur ^ 1], tid);
+      tb.store(lds_b[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue -------------------------------------------------------------------------
+  const int row_in_blk = 4 * (lane >> 5);
+  const int col_in_blk = lane & 31;
+  if constexpr (EPI == Epi::StoreBF16) {
+    __bf16* C = static_cast<__bf16*>(args.c);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WN + j * 32 + col_in_blk;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + row_in_blk + (r & 3);
+          if (m < args.M && n < args.N) C[int64_t(m) * args.ldc + n] = static_cast<__bf16>(acc[i][j][r]);
+        }
+      }
+  } else {
+    float* C = static_cast<float*>(args.c);
+    if (args.splits > 1) {
+      // publish this split's partial, then count arrivals; the last one reduces
+      constexpr int V = TM * TN * 4;                     // float4 per thread
+      const int tile = tm * args.tiles_n + tn;
+      float4* mine = reinterpret_cast<float4*>(args.ws) + (int64_t(tile) * args.splits + split) * V * NT;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            mine[((i * TN + j) * 4 + q) * NT + tid] =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      __threadfence();
+      __syncthreads();
+      if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(args.cnt + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = (prev == unsigned(args.splits - 1));
+      }
+      __syncthreads();
+      if (!last_flag) return;
+      __threadfence();
+      const float4* base = reinterpret_cast<const float4*>(args.ws) + int64_t(tile) * args.splits * V * NT;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int sp = 0; sp < args.splits; ++sp) {
+              float4 v;
+              if (sp == split)
+                v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+              else
+                v = base[(int64_t(sp) * V + (i * TN + j) * 4 + q) * NT + tid];
+              s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+            }
+            acc[i][j][4 * q] = s.x; acc[i][j][4 * q + 1] = s.y;
+            acc[i][j][4 * q + 2] = s.z; acc[i][j][4 * q + 3] = s.w;
+          }
+      if (tid == 0) __hip_atomic_store(args.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WN + j * 32 + col_in_blk;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + row_in_blk + (r & 3);
+          if (m < args.M && n < args.N) {
+            float* p = C + int64_t(m) * args.ldc + n;
+            *p = *p + acc[i][j][r];
+          }
+        }
+      }
+  }
+}
+
+__global__ void fill_zero_f32(float4* p, int64_t n4, float* tail, int ntail) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (blockIdx.x == 0 && int(threadIdx.x) < ntail) tail[threadIdx.x] = 0.f;
+}
+
+// ---- host side -------------------------------------------------------------------------------
+
+constexpr int64_t kMaxExtent = int64_t(1) << 31;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(int64_t T, int64_t in, int64_t out, int64_t mult) {
+  if (T < 0 || in < 0 || out < 0) return SL_EINVAL;
+  if (T >= kMaxExtent || in >= kMaxExtent || out >= kMaxExtent) return SL_ESHAPE;
+  if (in % mult || out % mult) return SL_ESHAPE;
+  // element offsets of every operand must fit the kernels' 64-bit row arithmetic and the
+  // 32-bit tile indices
+  return SL_OK;
+}
+
+// One tile configuration per launch shape.  256x256 with 4 waves (each a 128x128 wave tile of
+// 16 MFMA blocks) when the grid fills the chip; 128x128 otherwise.
+struct Shape {
+  int bm, bn;
+};
+
+Shape pick_shape(int64_t M, int64_t N) {
+  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big >= 200) return {256, 256};
+  return {128, 128};
+}
+
+// Split count for the weight gradient: fill ~256 CUs with output tiles, keep >= 8 k stages per
+// split.
+void pick_splits(int64_t M, int64_t N, int64_t K, Shape sh, int* splits, int* kps) {
+  const int64_t tiles = ((M + sh.bm - 1) / sh.bm) * ((N + sh.bn - 1) / sh.bn);
+  const int64_t nkt = (K + kBK - 1) / kBK;
+  int64_t s = 1;
+  if (tiles < 200) s = (256 + tiles / 2) / tiles;
+  if (s > nkt / 8) s = nkt / 8;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  int64_t per = (nkt + s - 1) / s;
+  if (per < 1) per = 1;
+  *kps = int(per);
+  *splits = int(nkt == 0 ? 1 : (nkt + per - 1) / per);
+}
+
+size_t wgrad_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const Shape sh = pick_shape(M, N);
+  int splits, kps;
+  pick_splits(M, N, K, sh, &splits, &kps);
+  if (splits <= 1) return 0;
+  const int64_t tiles = ((M + sh.bm - 1) / sh.bm) * ((N + sh.bn - 1) / sh.bn);
+  const int64_t part = tiles * splits * int64_t(sh.bm) * sh.bn * 4;
+  const int64_t cnt = ((tiles * 4 + 255) / 256) * 256;
+  return size_t(part + cnt);
+}
+
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, Elem EA, Elem EB, Epi EPI>
+int launch(hipStream_t st, Args& a) {
+  a.tiles_m = int((a.M + BM - 1) / BM);
+  a.tiles_n = int((a.N + BN - 1) / BN);
+  dim3 grid(a.tiles_m * a.tiles_n, 1, a.splits);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, 2, 2, A_KMAJ, B_KMAJ, EA, EB, EPI>), grid, dim3(256), 0, st, a);
+  return hipGetLastError() == hipSuccess ? SL_OK : SL_EHIP;
+}
+
+template <bool A_KMAJ, bool B_KMAJ, Elem EA, Elem EB, Epi EPI>
+int run(hipStream_t st, Args& a) {
+  const Shape sh = pick_shape(a.M, a.N);
+  if (sh.bm == 256) return launch<256, 256, A_KMAJ, B_KMAJ, EA, EB, EPI>(st, a);
+  return launch<128, 128, A_KMAJ, B_KMAJ, EA, EB, EPI>(st, a);
+}
+
+int wgrad_setup(Args& a, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes) {
+  const Shape sh = pick_shape(M, N);
+  int splits, kps;
+  pick_splits(M, N, K, sh, &splits, &kps);
+  a.splits = splits;
+  a.kt_per_split = kps;
+  if (splits > 1) {
+    const size_t need = wgrad_ws_bytes(M, N, K);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return SL_EWORKSPACE;
+    const int64_t tiles = ((M + sh.bm - 1) / sh.bm) * ((N + sh.bn - 1) / sh.bn);
+    a.ws = static_cast<float*>(ws);
+    a.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + tiles * splits * int64_t(sh.bm) * sh.bn * 4);
+  }
+  return SL_OK;
+}
+
+Args base_args(int64_t M, int64_t N, int64_t K) {
+  Args a{};
+  a.M = int(M); a.N = int(N); a.K = int(K);
+  a.splits = 1;
+  a.kt_per_split = int((K + kBK - 1) / kBK);
+  return a;
+}
+
+}  // namespace
+
+extern "C" int sl_grad_buffer_zero(void* stream, float* grad_data, int64_t numel) {
+  if (numel < 0) return SL_EINVAL;
+  if (numel == 0) return SL_OK;
+  if (!grad_data) return SL_EINVAL;
+  if (!aligned16(grad_data)) return SL_EALIGN;
+  const int64_t n4 = numel / 4;
+  const int ntail = int(numel - n4 * 4);
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(fill_zero_f32, dim3(unsigned(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     reinterpret_cast<float4*>(grad_data), n4, grad_data + n4 * 4, ntail);
+  return hipGetLastError() == hipSuccess ? SL_OK : SL_EHIP;
+}
+
+extern "C" int sl_linear_fwd(void* stream, const void* X, const void* W, void* Y, int64_t T, int64_t in,
+                             int64_t out) {
+  int st = check_dims(T, in, out, 8);
+  if (st) return st;
+  if (T == 0 || out == 0) return SL_OK;
+  if (!Y || (in > 0 && (!X || !W))) return SL_EINVAL;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return SL_EALIGN;
+  Args a = base_args(T, out, in);
+  a.a = {X, nullptr, in, int(T)};
+  a.b = {W, nullptr, in, int(out)};
+  a.c = Y;
+  a.ldc = out;
+  return run<true, true, Elem::BF16, Elem::BF16, Epi::StoreBF16>(static_cast<hipStream_t>(stream), a);
+}
+
+extern "C" int sl_linear_dgrad(void* stream, const void* dY, const void* W, void* dX, int64_t T, int64_t in,
+                               int64_t out) {
+  int st = check_dims(T, in, out, 8);
+  if (st) return st;
+  if (T == 0 || in == 0) return SL_OK;
+  if (!dX || (out > 0 && (!dY || !W))) return SL_EINVAL;
+  if (!aligned16(dY) || !aligned16(W) || !aligned16(dX)) return SL_EALIGN;
+  Args a = base_args(T, in, out);
+  a.a = {dY, nullptr, out, int(T)};
+  a.b = {W, nullptr, in, int(in)};
+  a.c = dX;
+  a.ldc = in;
+  return run<true, false, Elem::BF16, Elem::BF16, Epi::StoreBF16>(static_cast<hipStream_t>(stream), a);
+}
+
+extern "C" size_t sl_wgrad_workspace_bytes(int64_t T, int64_t in, int64_t out) {
+  if (T < 0 || in < 0 || out < 0) return 0;
+  return wgrad_ws_bytes(out, in, T);
+}
+
+extern "C" int sl_linear_wgrad_accum(void* stream, const void* X, const void* dY, float* main_grad, int64_t T,
+                                     int64_t in, int64_t out, void* workspace, size_t workspace_bytes) {
+  int st = check_dims(T, in, out, 8);
+  if (st) return st;
+  if (T == 0 || in == 0 || out == 0) return SL_OK;
+  if (!X || !dY || !main_grad) return SL_EINVAL;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(main_grad)) return SL_EALIGN;
+  Args a = base_args(out, in, T);
+  a.a = {dY, nullptr, out, int(out)};
+  a.b = {X, nullptr, in, int(in)};
+  a.c = main_grad;
+  a.ldc = in;
+  st = wgrad_setup(a, out, in, T, workspace, workspace_bytes);
+  if (st) return st;
+  return run<false, false, Elem::BF16, Elem::BF16, Epi::AccumF32>(static_cast<hipStream_t>(stream), a);
+}
+
+extern "C" int sl_linear_fwd_mxfp8(void* stream, const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
+                                   const uint8_t* Ws, void* Y, int64_t T, int64_t in, int64_t out) {
+  int st = check_dims(T, in, out, 8);
+  if (st) return st;
+  if (in % 32) return SL_ESHAPE;
+  if (T == 0 || out == 0) return SL_OK;
+  if (!Y || (in > 0 && (!Xq || !Xs || !Wq || !Ws))) return SL_EINVAL;
+  if (!aligned16(Xq) || !aligned16(Wq) || !aligned16(Y)) return SL_EALIGN;
+  Args a = base_args(T, out, in);
+  a.a = {Xq, Xs, in, int(T)};
+  a.b = {Wq, Ws, in, int(out)};
+  a.c = Y;
+  a.ldc = out;
+  return run<true, true, Elem::MXFP8, Elem::MXFP8, Epi::StoreBF16>(static_cast<hipStream_t>(stream), a);
+}
+
+extern "C" int sl_linear_dgrad_mxfp8w(void* stream, const void* dY, const uint8_t* Wq, const uint8_t* Ws,
+                                      void* dX, int64_t T, int64_t in, int64_t out) {
+  int st = check_dims(T, in, out, 8);
+  if (st) return st;
+  if (in % 32) return SL_ESHAPE;
+  if (T == 0 || in == 0) return SL_OK;
+  if (!dX || (out > 0 && (!dY || !Wq || !Ws))) return SL_EINVAL;
+  if (!aligned16(dY) || !aligned16(Wq) || !aligned16(dX)) return SL_EALIGN;
+  Args a = base_args(T, in, out);
+  a.a = {dY, nullptr, out, int(T)};
+  a.b = {Wq, Ws, in, int(in)};
+  a.c = dX;
+  a.ldc = in;
+  return run<true, false, Elem::BF16, Elem::MXFP8, Epi::StoreBF16>(static_cast<hipStream_t>(stream), a);
+}
+
+extern "C" int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, const uint8_t* Xs, const void* dY,
+                                            float* main_grad, int64_t T, int64_t in, int64_t out, void* workspace,
+                                            size_t workspace_bytes) {
+  int st = check_dims(T, in, out, 8);
+  if (st) return st;
+  if (in % 32) return SL_ESHAPE;
+  if (T == 0 || in == 0 || out == 0) return SL_OK;
+  if (!Xq || !Xs || !dY || !main_grad) return SL_EINVAL;
+  if (!aligned16(Xq) || !aligned16(dY) || !aligned16(main_grad)) return SL_EALIGN;
+  Args a = base_args(out, in, T);
+  a.a = {dY, nullptr, out, int(out)};
+  a.b = {Xq, Xs, in, int(in)};
+  a.c = main_grad;
+  a.ldc = in;
+  st = wgrad_setup(a, out, in, T, workspace, workspace_bytes);
+  if (st) return st;
+  return run<false, false, Elem::BF16, Elem::MXFP8, Epi::AccumF32>(static_cast<hipStream_t>(stream), a);
+}

@@ -1,0 +1,167 @@
+"""Thin torch binding of the C ABI: argument marshalling only, every step runs in the HIP library.
+
+Function names match the C entry points.  Tensors must be CUDA (HIP) tensors on one device,
+contiguous, with the dtypes of include/sharded_linear.h; work is enqueued on torch's current
+stream of that device.  Outputs not supplied are allocated with torch.empty (plumbing).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import check, lib
+
+BF16, F32, U8 = torch.bfloat16, torch.float32, torch.uint8
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _want(t, name, dtype, shape, dev):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _device(t):
+    if not t.is_cuda:
+        raise ValueError("the HIP library works on GPU tensors only; got a CPU tensor")
+    return t.device
+
+
+def sl_grad_buffer_zero(grad_data: torch.Tensor) -> torch.Tensor:
+    dev = _device(grad_data)
+    _want(grad_data, "grad_data", F32, (grad_data.numel(),), dev)
+    check("sl_grad_buffer_zero", lib().sl_grad_buffer_zero(_stream(dev), _ptr(grad_data), grad_data.numel()))
+    return grad_data
+
+
+def sl_linear_fwd(X: torch.Tensor, W: torch.Tensor, Y: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[T,out] = X[T,in] . W[out,in]^T (bf16)."""
+    dev = _device(X)
+    T, n_in = X.shape
+    n_out = W.shape[0]
+    _want(X, "X", BF16, (T, n_in), dev)
+    _want(W, "W", BF16, (n_out, n_in), dev)
+    if Y is None:
+        Y = torch.empty((T, n_out), dtype=BF16, device=dev)
+    _want(Y, "Y", BF16, (T, n_out), dev)
+    check("sl_linear_fwd", lib().sl_linear_fwd(_stream(dev), _ptr(X), _ptr(W), _ptr(Y), T, n_in, n_out))
+    return Y
+
+
+def sl_linear_dgrad(dY: torch.Tensor, W: torch.Tensor, dX: torch.Tensor | None = None) -> torch.Tensor:
+    """dX[T,in] = dY[T,out] . W[out,in] (bf16)."""
+    dev = _device(dY)
+    T, n_out = dY.shape
+    n_in = W.shape[1]
+    _want(dY, "dY", BF16, (T, n_out), dev)
+    _want(W, "W", BF16, (n_out, n_in), dev)
+    if dX is None:
+        dX = torch.empty((T, n_in), dtype=BF16, device=dev)
+    _want(dX, "dX", BF16, (T, n_in), dev)
+    check("sl_linear_dgrad", lib().sl_linear_dgrad(_stream(dev), _ptr(dY), _ptr(W), _ptr(dX), T, n_in, n_out))
+    return dX
+
+
+def sl_wgrad_workspace_bytes(T: int, n_in: int, n_out: int) -> int:
+    return int(lib().sl_wgrad_workspace_bytes(T, n_in, n_out))
+
+
+_WS = {}
+
+
+def wgrad_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
+    """A zero-initialised workspace of at least ``nbytes`` for the current stream of ``dev``.
+
+    The kernels return the workspace's counters to zero after every call, so one buffer per
+    stream is reused; it only grows (a fresh zero buffer) when a larger size is asked for.
+    """
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=U8, device=dev)
+        _WS[key] = ws
+    return ws
+
+
+def sl_linear_wgrad_accum(X: torch.Tensor, dY: torch.Tensor, main_grad: torch.Tensor,
+                          workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """main_grad[out,in] += dY[T,out]^T . X[T,in] in fp32, in place."""
+    dev = _device(X)
+    T, n_in = X.shape
+    n_out = dY.shape[1]
+    _want(X, "X", BF16, (T, n_in), dev)
+    _want(dY, "dY", BF16, (T, n_out), dev)
+    _want(main_grad, "main_grad", F32, (n_out, n_in), dev)
+    need = sl_wgrad_workspace_bytes(T, n_in, n_out)
+    if workspace is None:
+        workspace = wgrad_workspace(dev, need) if need else None
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check("sl_linear_wgrad_accum", lib().sl_linear_wgrad_accum(
+        _stream(dev), _ptr(X), _ptr(dY), _ptr(main_grad), T, n_in, n_out, _ptr(workspace), nbytes))
+    return main_grad
+
+
+def sl_linear_fwd_mxfp8(Xq, Xs, Wq, Ws, Y=None):
+    """Y = deq(Xq, Xs) . deq(Wq, Ws)^T (bf16 out); codes and scales are uint8."""
+    dev = _device(Xq)
+    T, n_in = Xq.shape
+    n_out = Wq.shape[0]
+    _want(Xq, "Xq", U8, (T, n_in), dev)
+    _want(Xs, "Xs", U8, (T, n_in // 32), dev)
+    _want(Wq, "Wq", U8, (n_out, n_in), dev)
+    _want(Ws, "Ws", U8, (n_out, n_in // 32), dev)
+    if Y is None:
+        Y = torch.empty((T, n_out), dtype=BF16, device=dev)
+    _want(Y, "Y", BF16, (T, n_out), dev)
+    check("sl_linear_fwd_mxfp8", lib().sl_linear_fwd_mxfp8(
+        _stream(dev), _ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(Y), T, n_in, n_out))
+    return Y
+
+
+def sl_linear_dgrad_mxfp8w(dY, Wq, Ws, dX=None):
+    """dX = dY . deq(Wq, Ws) (bf16 in/out)."""
+    dev = _device(dY)
+    T, n_out = dY.shape
+    n_in = Wq.shape[1]
+    _want(dY, "dY", BF16, (T, n_out), dev)
+    _want(Wq, "Wq", U8, (n_out, n_in), dev)
+    _want(Ws, "Ws", U8, (n_out, n_in // 32), dev)
+    if dX is None:
+        dX = torch.empty((T, n_in), dtype=BF16, device=dev)
+    _want(dX, "dX", BF16, (T, n_in), dev)
+    check("sl_linear_dgrad_mxfp8w", lib().sl_linear_dgrad_mxfp8w(
+        _stream(dev), _ptr(dY), _ptr(Wq), _ptr(Ws), _ptr(dX), T, n_in, n_out))
+    return dX
+
+
+def sl_linear_wgrad_accum_mxfp8x(Xq, Xs, dY, main_grad, workspace=None):
+    """main_grad += dY^T . deq(Xq, Xs) in fp32, in place."""
+    dev = _device(Xq)
+    T, n_in = Xq.shape
+    n_out = dY.shape[1]
+    _want(Xq, "Xq", U8, (T, n_in), dev)
+    _want(Xs, "Xs", U8, (T, n_in // 32), dev)
+    _want(dY, "dY", BF16, (T, n_out), dev)
+    _want(main_grad, "main_grad", F32, (n_out, n_in), dev)
+    need = sl_wgrad_workspace_bytes(T, n_in, n_out)
+    if workspace is None:
+        workspace = wgrad_workspace(dev, need) if need else None
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check("sl_linear_wgrad_accum_mxfp8x", lib().sl_linear_wgrad_accum_mxfp8x(
+        _stream(dev), _ptr(Xq), _ptr(Xs), _ptr(dY), _ptr(main_grad), T, n_in, n_out, _ptr(workspace), nbytes))
+    return main_grad

@@ -66,36 +66,6 @@ def normal_bf16(shape, seed: int, std: float = 1.0) -> np.ndarray:
     return f32_to_bf16_bits(normal_f32(shape, seed, std))
 
 
-def _round_to_e4m3_grid(a: np.ndarray) -> np.ndarray:
-    """Round non-negative float64 magnitudes to the E4M3FN value grid (RNE), saturating at 448."""
-    out = np.zeros_like(a)
-    nz = a > 0
-    v = a[nz]
-    e = np.floor(np.log2(v))
-    e = np.maximum(e, _E4M3_EMIN)
-    step = np.exp2(e - 3)                     # 3 mantissa bits
-    r = np.rint(v / step) * step              # numpy rint rounds half to even
-    out[nz] = np.minimum(r, _E4M3_MAX)
-    return out
-
-
-def _encode_e4m3(mag: np.ndarray, neg: np.ndarray) -> np.ndarray:
-    """Bit-encode grid magnitudes (exact E4M3 values) into uint8 codes."""
-    code = np.zeros(mag.shape, dtype=np.uint8)
-    nz = mag > 0
-    v = mag[nz]
-    e = np.floor(np.log2(v))
-    sub = e < _E4M3_EMIN
-    ef = np.where(sub, 0, e + 7).astype(np.int64)
-    mant = np.where(sub, v / 2.0 ** -9, v / np.exp2(e) * 8 - 8)
-    m = np.rint(mant).astype(np.int64)
-    assert np.all(np.abs(mant - m) == 0), "magnitude not on the E4M3 grid"
-    assert np.all((m >= 0) & (m <= 7)) and np.all(ef <= 15)
-    code[nz] = (ef << 3 | m).astype(np.uint8)
-    code[neg] |= np.uint8(0x80)
-    return code
-
-
 def mxfp8_quantize(x: np.ndarray):
     """Quantise float32 ``x`` (last axis a multiple of 32) to MXFP8 E4M3 with E8M0 block scales.
 
@@ -104,23 +74,47 @@ def mxfp8_quantize(x: np.ndarray):
       [-127, 127], stored biased by 127; an all-zero block stores 0 and zero codes;
       elements x / 2^X are rounded to nearest-even on the E4M3 grid, saturating at +-448.
     Returns (codes uint8 same shape as x, scales uint8 shape [..., K/32]).
+    Works on float32 bit fields: floor(log2) of a normal float32 is its exponent field, and
+    dividing by 2^X is exact for the inputs this module draws (no float32 subnormals arise).
     """
-    x = np.asarray(x, dtype=np.float32)
+    x = np.ascontiguousarray(x, dtype=np.float32)
     k = x.shape[-1]
     if k % MX_BLOCK:
         raise ValueError("last axis must be a multiple of 32")
-    xb = x.astype(np.float64).reshape(*x.shape[:-1], k // MX_BLOCK, MX_BLOCK)
-    if not np.all(np.isfinite(xb)):
+    if not np.all(np.isfinite(x)):
         raise ValueError("MXFP8 quantiser takes finite inputs only")
+    xb = x.reshape(-1, k // MX_BLOCK, MX_BLOCK)
     amax = np.abs(xb).max(axis=-1)
-    with np.errstate(divide="ignore"):
-        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - _E4M3_EMAX, -127)
+    if np.any((amax > 0) & (amax < np.float32(2.0 ** -126))):
+        raise ValueError("float32 subnormal block maxima are not supported")
+    e = (amax.view(np.int32) >> 23).astype(np.int32) - 127 - _E4M3_EMAX       # floor(log2 amax) - 8
     e = np.clip(e, -127, 127)
-    scales = np.where(amax > 0, e + 127, 0).astype(np.uint8)
-    scaled = xb / np.exp2(e)[..., None]
-    mag = _round_to_e4m3_grid(np.abs(scaled))
-    codes = _encode_e4m3(mag, np.signbit(scaled))
-    return codes.reshape(x.shape), scales
+    zero_blk = amax == 0
+    scales = np.where(zero_blk, 0, e + 127).astype(np.uint8)
+    # multiply by 2^-X, built as an exact float32 power of two (X in [-127, 127] -> two factors)
+    e1 = np.clip(-e, -126, 127)
+    e2 = -e - e1
+    f1 = ((e1 + 127).astype(np.int32) << 23).view(np.float32)
+    f2 = ((e2 + 127).astype(np.int32) << 23).view(np.float32)
+    v = xb * f1[..., None] * f2[..., None]
+    a = np.abs(v)
+    bits = a.view(np.uint32)
+    # normals of E4M3 (a >= 2^-6): round the float32 mantissa to 3 bits, nearest-even
+    rb = (bits + np.uint32(0x7FFFF) + ((bits >> np.uint32(20)) & np.uint32(1))) & np.uint32(0xFFF00000)
+    rn = rb.view(np.float32)
+    # subnormals of E4M3 (a < 2^-6): a fixed step 2^-9, nearest-even
+    rs = np.rint(a * np.float32(512.0)) * np.float32(1.0 / 512.0)
+    r = np.where(a < np.float32(2.0 ** -6), rs, rn)
+    r = np.minimum(r, np.float32(_E4M3_MAX))
+    rbits = r.view(np.uint32)
+    ef = ((rbits >> np.uint32(23)) & np.uint32(0xFF)).astype(np.int32) - 127 + 7
+    normal = r >= np.float32(2.0 ** -6)
+    code_n = (np.clip(ef, 0, 15).astype(np.uint32) << np.uint32(3)) | ((rbits >> np.uint32(20)) & np.uint32(7))
+    code_s = (r * np.float32(512.0)).astype(np.uint32)        # 0..8; 8 is the code of 2^-6
+    code = np.where(normal, code_n, code_s).astype(np.uint8)
+    code |= (np.signbit(v).astype(np.uint8) << np.uint8(7))
+    code[zero_blk] = 0
+    return code.reshape(x.shape), scales.reshape(*x.shape[:-1], k // MX_BLOCK)
 
 
 def mxfp8_normal(shape, seed: int, std: float = 1.0):

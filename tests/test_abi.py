@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every declared symbol, and validates arguments on the host.
+
+No call here reaches a kernel launch: each one fails validation (or is a zero-extent no-op)
+before any HIP call, so these run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sharded_linear_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sharded_linear.h")
+
+SL_OK, SL_EINVAL, SL_EALIGN, SL_ESHAPE, SL_EWORKSPACE = 0, -1, -2, -3, -4
+A = 1 << 20          # an aligned fake device address, never dereferenced
+MIS = A + 2          # misaligned
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sl_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    L = _lib.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(syms) == set(_lib.PROTOTYPES), "ctypes prototypes must mirror the header"
+
+
+def test_single_hip_runtime():
+    _lib.lib()
+    assert len(_lib.hip_runtimes_mapped()) <= 1
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert L.sl_status_str(st).decode().startswith("SL_")
+    assert L.sl_status_str(12345) == b"unknown status"
+
+
+@pytest.mark.parametrize("fn", ["sl_linear_fwd", "sl_linear_dgrad"])
+def test_gemm_validation(fn):
+    f = getattr(_lib.lib(), fn)
+    assert f(None, A, A, A, 16, 12, 16) == SL_ESHAPE          # in not a multiple of 8
+    assert f(None, A, A, A, 16, 16, 20) == SL_ESHAPE          # out not a multiple of 8
+    assert f(None, A, A, A, -1, 16, 16) == SL_EINVAL
+    assert f(None, A, A, A, 1 << 31, 16, 16) == SL_ESHAPE
+    assert f(None, A, MIS, A, 16, 16, 16) == SL_EALIGN
+    assert f(None, A, A, MIS, 16, 16, 16) == SL_EALIGN
+    assert f(None, None, A, A, 16, 16, 16) == SL_EINVAL
+    assert f(None, A, A, None, 16, 16, 16) == SL_EINVAL
+    assert f(None, None, None, None, 0, 16, 16) == SL_OK       # empty: nothing to do
+
+
+def test_wgrad_validation():
+    f = _lib.lib().sl_linear_wgrad_accum
+    assert f(None, A, A, A, 16, 12, 16, None, 0) == SL_ESHAPE
+    assert f(None, MIS, A, A, 16, 16, 16, None, 0) == SL_EALIGN
+    assert f(None, A, A, MIS, 16, 16, 16, None, 0) == SL_EALIGN
+    assert f(None, A, None, A, 16, 16, 16, None, 0) == SL_EINVAL
+    assert f(None, None, None, None, 0, 16, 16, None, 0) == SL_OK   # T = 0 leaves main_grad as is
+    # a shape that needs split-K partials refuses a missing or short workspace
+    T, n_in, n_out = 8192, 1024, 2048
+    need = _lib.lib().sl_wgrad_workspace_bytes(T, n_in, n_out)
+    assert need > 0
+    assert f(None, A, A, A, T, n_in, n_out, None, 0) == SL_EWORKSPACE
+    assert f(None, A, A, A, T, n_in, n_out, A, need - 256) == SL_EWORKSPACE
+    assert f(None, A, A, A, T, n_in, n_out, MIS, need) == SL_EWORKSPACE
+    assert _lib.lib().sl_wgrad_workspace_bytes(0, 16, 16) == 0
+
+
+def test_mxfp8_validation():
+    L = _lib.lib()
+    assert L.sl_linear_fwd_mxfp8(None, A, A, A, A, A, 16, 48, 16) == SL_ESHAPE     # in % 32
+    assert L.sl_linear_dgrad_mxfp8w(None, A, A, A, A, 16, 48, 16) == SL_ESHAPE
+    assert L.sl_linear_wgrad_accum_mxfp8x(None, A, A, A, A, 16, 48, 16, None, 0) == SL_ESHAPE
+    assert L.sl_linear_fwd_mxfp8(None, A, None, A, A, A, 16, 64, 16) == SL_EINVAL   # no scales
+    assert L.sl_linear_fwd_mxfp8(None, MIS, A, A, A, A, 16, 64, 16) == SL_EALIGN
+    assert L.sl_linear_wgrad_accum_mxfp8x(None, A, A, A, None, 16, 64, 16, None, 0) == SL_EINVAL
+    assert L.sl_linear_fwd_mxfp8(None, None, None, None, None, None, 0, 64, 16) == SL_OK
+
+
+def test_zero_fill_validation():
+    L = _lib.lib()
+    assert L.sl_grad_buffer_zero(None, A, -1) == SL_EINVAL
+    assert L.sl_grad_buffer_zero(None, None, 10) == SL_EINVAL
+    assert L.sl_grad_buffer_zero(None, MIS, 10) == SL_EALIGN
+    assert L.sl_grad_buffer_zero(None, None, 0) == SL_OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    from sharded_linear_amd import sl_linear_fwd
+    with pytest.raises(ValueError):
+        sl_linear_fwd(torch.zeros(4, 8, dtype=torch.bfloat16), torch.zeros(8, 8, dtype=torch.bfloat16))

@@ -342,3 +342,42 @@ def test_layout_properties_random(seed):
             assert all(e - off < bs for e in before)   # ... and not earlier
         prev = off + num
     assert lay.numel == prev
+
+
+def _scalar_e4m3_quant(block):
+    """One block by the OCP MX rule, element by element in Python floats (test reference)."""
+    amax = max(abs(float(v)) for v in block)
+    if amax == 0:
+        return [0] * len(block), 0
+    X = min(max(math.floor(math.log2(amax)) - 8, -127), 127)
+    grid = sorted({numerics.e4m3_value(c) for c in range(0x7F)})          # non-negative values
+    codes = []
+    for v in block:
+        a = abs(float(v)) / 2.0 ** X
+        if a >= 448:
+            r = 448.0
+        else:
+            hi = next(g for g in grid if g >= a)
+            lo = max(g for g in grid if g <= a)
+            if hi - a < a - lo:
+                r = hi
+            elif a - lo < hi - a:
+                r = lo
+            else:                                                           # tie: even code
+                cl, ch = grid.index(lo), grid.index(hi)
+                r = lo if cl % 2 == 0 else hi
+        c = grid.index(r) | (0x80 if math.copysign(1, float(v)) < 0 else 0)
+        codes.append(c)
+    return codes, X + 127
+
+
+def test_quantiser_matches_scalar_rule():
+    rng = np.random.default_rng(8)
+    blocks = [rng.standard_normal(32).astype(np.float32) * np.float32(s) for s in (1, 0.02, 3e-3, 7e4)]
+    tie = np.array([1.0, 1.0625, 1.1875, 0.25 + 2 ** -11, 2 ** -14, 2 ** -16 * 3] + [0.5] * 26, np.float32)
+    blocks += [tie, -tie, np.full(32, 460.0, np.float32), np.zeros(32, np.float32)]
+    x = np.stack(blocks)
+    q, s = synth.mxfp8_quantize(x)
+    for b in range(x.shape[0]):
+        codes, sc = _scalar_e4m3_quant(x[b])
+        assert s[b, 0] == sc and list(q[b]) == codes, b

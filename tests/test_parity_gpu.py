@@ -1,0 +1,326 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle.
+
+Bars: max|gpu - ref| / max|ref| <= 4e-3 for bf16 outputs (Y, dX) and <= 1e-4 for the fp32
+main_grad, per tensor; layouts, padding and untouched neighbours are compared bit-exactly.
+Small cases are compared element by element; the full-size workloads on sampled rows and
+entries that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import linear as ol
+from oracle import layout as olayout
+from synth import configs
+from tests.gpu_util import dev_bf16, dev_u8, host_bits, host_f64, say
+
+import sharded_linear_amd as sl
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 4e-3
+TOL_F32 = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    sl.sl_linear_fwd  # noqa: B018
+    yield
+    torch.cuda.synchronize()
+
+
+def rand_case(T, n_in, n_out, seed):
+    X = synth.normal_bf16((T, n_in), seed * 10 + 1)
+    W = synth.normal_bf16((n_out, n_in), seed * 10 + 0, synth.W_STD)
+    dY = synth.normal_bf16((T, n_out), seed * 10 + 2)
+    return X, W, dY
+
+
+# shapes: (T, in, out) -- ragged tails in every dimension, the 128- and 256-tile configurations,
+# split-K and unsplit weight gradients, minimum extents
+SMALL = [
+    (1, 8, 8), (7, 24, 40), (128, 256, 512), (300, 264, 520), (513, 1032, 776),
+    (4104, 264, 520), (1000, 2056, 264), (4100, 264, 3336), (3333, 3336, 4104),
+]
+
+
+@pytest.mark.parametrize("T,n_in,n_out", SMALL)
+def test_fwd_dgrad_wgrad_elementwise(T, n_in, n_out):
+    say(f"case T={T} in={n_in} out={n_out}")
+    X, W, dY = rand_case(T, n_in, n_out, T + n_in + n_out)
+    G0 = synth.normal_f32((n_out, n_in), 99)
+    Xd, Wd, dYd = dev_bf16(X), dev_bf16(W), dev_bf16(dY)
+    Gd = torch.from_numpy(G0).cuda()
+    Y = sl.sl_linear_fwd(Xd, Wd)
+    dX = sl.sl_linear_dgrad(dYd, Wd)
+    sl.sl_linear_wgrad_accum(Xd, dYd, Gd)
+    torch.cuda.synchronize()
+    e_y = ol.rel_err(host_f64(Y), ol.linear_fwd(X, W))
+    e_dx = ol.rel_err(host_f64(dX), ol.linear_dgrad(dY, W))
+    e_g = ol.rel_err(host_f64(Gd), ol.linear_wgrad_accum(G0, X, dY))
+    say(f"  rel err Y {e_y:.2e} dX {e_dx:.2e} main_grad {e_g:.2e} ws={sl.sl_wgrad_workspace_bytes(T, n_in, n_out)}")
+    assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
+
+
+def test_c1_two_microbatches_into_buffer_view():
+    w = configs.WORKLOADS["c1"]
+    say("case c1")
+    buf = sl.ParamAndGradBuffer({"weight": (512, 256)}, "cuda", bucket_size=None)
+    assert buf.numel == 131072 and buf.numel % 64 == 0 and buf.index["weight"][:2] == (0, 131072)
+    W = configs.weight(w, "weight")
+    buf.param("weight").copy_(dev_bf16(W))
+    buf.zero_grad_buffer()
+    Xs = [configs.x(w, "weight", k) for k in range(2)]
+    dYs = [configs.dy(w, "weight", k) for k in range(2)]
+    Ys, dXs = [], []
+    for X, dY in zip(Xs, dYs):
+        Ys.append(sl.sl_linear_fwd(dev_bf16(X), buf.param("weight")))
+        dXs.append(sl.sl_linear_dgrad(dev_bf16(dY), buf.param("weight")))
+        sl.sl_linear_wgrad_accum(dev_bf16(X), dev_bf16(dY), buf.main_grad("weight"))
+    torch.cuda.synchronize()
+    rY, rdX, rG = ol.step(W, Xs, dYs)
+    for k in range(2):
+        assert ol.rel_err(host_f64(Ys[k]), rY[k]) <= TOL_BF16
+        assert ol.rel_err(host_f64(dXs[k]), rdX[k]) <= TOL_BF16
+    assert ol.rel_err(host_f64(buf.main_grad("weight")), rG) <= TOL_F32
+    # same data twice: a deterministic kernel gives exactly twice the single accumulation
+    buf.zero_grad_buffer()
+    sl.sl_linear_wgrad_accum(dev_bf16(Xs[0]), dev_bf16(dYs[0]), buf.main_grad("weight"))
+    torch.cuda.synchronize()
+    once = buf.main_grad("weight").clone()
+    sl.sl_linear_wgrad_accum(dev_bf16(Xs[0]), dev_bf16(dYs[0]), buf.main_grad("weight"))
+    torch.cuda.synchronize()
+    assert torch.equal(buf.main_grad("weight"), 2 * once)
+
+
+def test_exact_special_cases_bitwise():
+    say("case exact special cases")
+    rng = np.random.default_rng(5)
+    T, n_in, n_out = 96, 264, 136
+    W = synth.normal_bf16((n_out, n_in), 5, 1.0)
+    X = np.zeros((T, n_in), np.float32)
+    cols = rng.integers(0, n_in, size=T)
+    X[np.arange(T), cols] = 1.0
+    Y = host_f64(sl.sl_linear_fwd(dev_bf16(synth.f32_to_bf16_bits(X)), dev_bf16(W)))
+    Wf = ol.linear_fwd(np.eye(n_in), W)          # = W^T as float64, exact
+    assert np.array_equal(Y, Wf[cols])            # row t of Y is column cols[t] of W
+    dY = np.zeros((T, n_out), np.float32)
+    rows = rng.integers(0, n_out, size=T)
+    dY[np.arange(T), rows] = 1.0
+    dX = host_f64(sl.sl_linear_dgrad(dev_bf16(synth.f32_to_bf16_bits(dY)), dev_bf16(W)))
+    assert np.array_equal(dX, ol.linear_dgrad(np.eye(n_out), W)[rows])
+    # T = 1: the wgrad is an outer product of bf16 values, exact in fp32
+    x1 = synth.normal_bf16((1, n_in), 6)
+    g1 = synth.normal_bf16((1, n_out), 7)
+    G = torch.zeros((n_out, n_in), dtype=torch.float32, device="cuda")
+    sl.sl_linear_wgrad_accum(dev_bf16(x1), dev_bf16(g1), G)
+    assert np.array_equal(host_f64(G), ol.linear_wgrad(x1, g1))
+
+
+def test_empty_and_degenerate():
+    say("case empty and degenerate")
+    W = dev_bf16(synth.normal_bf16((16, 8), 1))
+    X0 = torch.empty((0, 8), dtype=torch.bfloat16, device="cuda")
+    dY0 = torch.empty((0, 16), dtype=torch.bfloat16, device="cuda")
+    assert sl.sl_linear_fwd(X0, W).shape == (0, 16)
+    assert sl.sl_linear_dgrad(dY0, W).shape == (0, 8)
+    G = torch.full((16, 8), 3.0, device="cuda")
+    sl.sl_linear_wgrad_accum(X0, dY0, G)        # T = 0 leaves main_grad as it was
+    torch.cuda.synchronize()
+    assert torch.equal(G, torch.full((16, 8), 3.0, device="cuda"))
+
+
+def test_neighbours_and_padding_untouched():
+    """A wgrad into one view of grad_data leaves every other element bit-identical."""
+    say("case neighbours and padding")
+    shapes = {"a": (136, 264), "b": (520, 264), "c": (8, 8)}
+    buf = sl.ParamAndGradBuffer(shapes, "cuda", bucket_size=None)
+    ref = olayout.build_layout([136 * 264, 520 * 264, 64], bucket_size=None)
+    assert [buf.index[k][:2] for k in shapes] == list(zip(ref.start, ref.end)) and buf.numel == ref.numel
+    sentinel = torch.full((buf.numel,), -7.25, device="cuda")
+    buf.grad_data.copy_(sentinel)
+    X, W, dY = rand_case(4104, 264, 520, 3)       # split-K path
+    sl.sl_linear_wgrad_accum(dev_bf16(X), dev_bf16(dY), buf.main_grad("b"))
+    torch.cuda.synchronize()
+    s, e, _ = buf.index["b"]
+    g = buf.grad_data
+    assert torch.equal(g[:s], sentinel[:s]) and torch.equal(g[e:], sentinel[e:])
+    want = ol.linear_wgrad_accum(np.full((520, 264), -7.25), X, dY)
+    assert ol.rel_err(host_f64(buf.main_grad("b")), want) <= TOL_F32
+
+
+def test_wgrad_is_deterministic():
+    say("case determinism")
+    X, W, dY = rand_case(8192, 1024, 2048, 11)   # split-K path at a C3-like shape
+    Xd, dYd = dev_bf16(X), dev_bf16(dY)
+    outs = []
+    for _ in range(3):
+        G = torch.zeros((2048, 1024), device="cuda")
+        sl.sl_linear_wgrad_accum(Xd, dYd, G)
+        outs.append(G)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_grad_buffer_zero_fill():
+    say("case zero fill")
+    for n in (1, 3, 4, 1023, 1 << 20, (1 << 20) + 5):
+        g = torch.full((n,), 5.0, device="cuda")
+        sl.sl_grad_buffer_zero(g)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(g)) == 0
+
+
+def test_autograd_glue():
+    """forward saves (input, weight); backward returns dX and no weight grad, fills main_grad."""
+    say("case autograd")
+    buf = sl.ParamAndGradBuffer({"fc1": (264, 136), "fc2": (136, 264)}, "cuda", bucket_size=None)
+    W1 = synth.normal_bf16((264, 136), 1, synth.W_STD)
+    W2 = synth.normal_bf16((136, 264), 2, synth.W_STD)
+    p1 = buf.attach("fc1", torch.nn.Parameter(dev_bf16(W1).clone()))
+    p2 = buf.attach("fc2", torch.nn.Parameter(dev_bf16(W2).clone()))
+    assert p1.data_ptr() == buf.param("fc1").data_ptr()
+    X = synth.normal_bf16((4, 50, 136), 3)        # [s, b, h]
+    dY = synth.normal_bf16((4, 50, 136), 4)
+    x = dev_bf16(X).requires_grad_(True)
+    z = sl.linear_with_grad_accumulation(x, p1)
+    y = sl.linear_with_grad_accumulation(z, p2)
+    y.backward(dev_bf16(dY))
+    torch.cuda.synchronize()
+    assert p1.grad is None and p2.grad is None
+    assert p1.grad_added_to_main_grad and p2.grad_added_to_main_grad
+    Zr = ol.linear_fwd(X.reshape(200, 136), W1)
+    Zb = synth.f32_to_bf16_bits(host_f64(z).reshape(200, 264).astype(np.float32))   # what fc2 saw
+    assert ol.rel_err(host_f64(z).reshape(200, 264), Zr) <= TOL_BF16
+    assert ol.rel_err(host_f64(y).reshape(200, 136), ol.linear_fwd(Zb, W2)) <= TOL_BF16
+    dZ = ol.linear_dgrad(dY.reshape(200, 136), W2)
+    assert ol.rel_err(host_f64(buf.main_grad("fc2")), ol.linear_wgrad(Zb, dY.reshape(200, 136))) <= TOL_F32
+    dZb = host_f64(torch.autograd.grad(y, z, dev_bf16(dY), retain_graph=False)[0]) if False else None
+    assert dZb is None
+    assert ol.rel_err(host_f64(x.grad).reshape(200, 136), ol.linear_dgrad(dZ, W1)) <= 1e-2
+
+
+# ---------------------------------------------------------------------------------------------
+# MXFP8 operand variants
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,n_in,n_out", [(1, 32, 8), (300, 288, 520), (4104, 256, 520), (4100, 288, 3336)])
+def test_mxfp8_elementwise(T, n_in, n_out):
+    say(f"case mxfp8 T={T} in={n_in} out={n_out}")
+    Xq, Xs = synth.mxfp8_normal((T, n_in), 21)
+    Wq, Ws = synth.mxfp8_normal((n_out, n_in), 22, synth.W_STD)
+    dY = synth.normal_bf16((T, n_out), 23)
+    G0 = synth.normal_f32((n_out, n_in), 24)
+    Y = sl.sl_linear_fwd_mxfp8(dev_u8(Xq), dev_u8(Xs), dev_u8(Wq), dev_u8(Ws))
+    dX = sl.sl_linear_dgrad_mxfp8w(dev_bf16(dY), dev_u8(Wq), dev_u8(Ws))
+    G = torch.from_numpy(G0).cuda()
+    sl.sl_linear_wgrad_accum_mxfp8x(dev_u8(Xq), dev_u8(Xs), dev_bf16(dY), G)
+    torch.cuda.synchronize()
+    e_y = ol.rel_err(host_f64(Y), ol.linear_fwd_mxfp8(Xq, Xs, Wq, Ws))
+    e_dx = ol.rel_err(host_f64(dX), ol.linear_dgrad_mxfp8w(dY, Wq, Ws))
+    e_g = ol.rel_err(host_f64(G), ol.linear_wgrad_accum_mxfp8x(G0, Xq, Xs, dY))
+    say(f"  rel err Y {e_y:.2e} dX {e_dx:.2e} main_grad {e_g:.2e}")
+    assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
+
+
+def test_mxfp8_all_codes_decode_exactly():
+    """Every finite E4M3 code under several scales: a one-hot fwd returns the decoded value."""
+    say("case mxfp8 decode table")
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)   # 254 codes
+    n_out = 256
+    Wq = np.zeros((n_out, 32), np.uint8)
+    Wq[: codes.size, 0] = codes
+    for s in (100, 120, 127, 135):
+        Ws = np.full((n_out, 1), s, np.uint8)
+        Xq = np.zeros((1, 32), np.uint8); Xq[0, 0] = 0x38                            # 1.0
+        Xs = np.full((1, 1), 127, np.uint8)
+        Y = host_f64(sl.sl_linear_fwd_mxfp8(dev_u8(Xq), dev_u8(Xs), dev_u8(Wq), dev_u8(Ws)))[0]
+        want = ol.linear_fwd_mxfp8(Xq, Xs, Wq, Ws)[0]
+        assert np.array_equal(Y, want), s
+
+
+# ---------------------------------------------------------------------------------------------
+# Full-size workloads (launch configuration of the benchmark), sampled against the oracle
+# ---------------------------------------------------------------------------------------------
+
+def _sample_rows(n, k, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, size=k)]))
+
+
+def run_workload_sampled(key, mbs=None):
+    w = configs.WORKLOADS[key]
+    mbs = w.microbatches if mbs is None else mbs
+    buf = sl.ParamAndGradBuffer(w.params, "cuda")
+    ref = olayout.build_layout([o * i for o, i in w.params.values()], bucket_size=olayout.default_bucket_size(1))
+    for j, name in enumerate(w.params):
+        assert buf.index[name] == (ref.start[j], ref.end[j], ref.bucket_id[j])
+    assert buf.numel == ref.numel
+    buf.zero_grad_buffer()
+    weights = {}
+    for name in w.step_params:
+        wt = configs.weight(w, name)
+        weights[name] = wt
+        if not w.mxfp8:
+            buf.param(name).copy_(dev_bf16(wt))
+    # accumulators of the sampled reference entries
+    samples = {}
+    for name in w.step_params:
+        o, i = w.params[name]
+        rng = np.random.default_rng(7)
+        samples[name] = (rng.integers(0, o, 256), rng.integers(0, i, 256), np.zeros(256))
+    errs = []
+    for k in range(mbs):
+        for name in w.step_params:
+            o, i = w.params[name]
+            say(f"  {key} mb={k} {name} [{o},{i}]")
+            xk, dyk = configs.x(w, name, k), configs.dy(w, name, k)
+            rows = _sample_rows(w.tokens, 48, k)
+            if w.mxfp8:
+                (Xq, Xs), (Wq, Ws) = xk, weights[name]
+                Wqd, Wsd = dev_u8(Wq), dev_u8(Ws)
+                Y = sl.sl_linear_fwd_mxfp8(dev_u8(Xq), dev_u8(Xs), Wqd, Wsd)
+                dX = sl.sl_linear_dgrad_mxfp8w(dev_bf16(dyk), Wqd, Wsd)
+                sl.sl_linear_wgrad_accum_mxfp8x(dev_u8(Xq), dev_u8(Xs), dev_bf16(dyk), buf.main_grad(name))
+                Yr = ol.linear_fwd_mxfp8(Xq[rows], Xs[rows], Wq, Ws)
+                dXr = ol.linear_dgrad_mxfp8w(dyk[rows], Wq, Ws)
+                xf = ol.mxfp8_dequant(Xq, Xs)
+            else:
+                Wd = buf.param(name)
+                Xd = dev_bf16(xk)
+                dYd = dev_bf16(dyk)
+                Y = sl.sl_linear_fwd(Xd, Wd)
+                dX = sl.sl_linear_dgrad(dYd, Wd)
+                sl.sl_linear_wgrad_accum(Xd, dYd, buf.main_grad(name))
+                Yr = ol.linear_fwd(xk[rows], weights[name])
+                dXr = ol.linear_dgrad(dyk[rows], weights[name])
+                xf = ol._f64(xk)
+            torch.cuda.synchronize()
+            errs.append(ol.rel_err(host_f64(Y[torch.from_numpy(rows).cuda()]), Yr))
+            errs.append(ol.rel_err(host_f64(dX[torch.from_numpy(rows).cuda()]), dXr))
+            so, si, acc = samples[name]
+            dyf = ol._f64(dyk)
+            acc += np.einsum("tk,tk->k", dyf[:, so], xf[:, si])
+            assert errs[-1] <= TOL_BF16 and errs[-2] <= TOL_BF16, (key, k, name, errs[-2:])
+    for name in w.step_params:
+        so, si, acc = samples[name]
+        got = host_f64(buf.main_grad(name))[so, si]
+        e = ol.rel_err(got, acc)
+        say(f"  {key} {name} main_grad sampled rel err {e:.2e}")
+        assert e <= TOL_F32
+    # padding and the grad views of params outside the step stay zero
+    g = buf.grad_data
+    covered = torch.zeros(buf.numel, dtype=torch.bool, device="cuda")
+    for name in w.step_params:
+        s, e, _ = buf.index[name]
+        covered[s:e] = True
+    assert int(torch.count_nonzero(g[~covered])) == 0
+    say(f"  {key} max bf16 sampled rel err {max(errs):.2e}")
+
+
+@pytest.mark.parametrize("key", ["c2", "c3", "c4", "c5"])
+def test_full_size_workload_sampled(key):
+    say(f"case workload {key}")
+    run_workload_sampled(key, mbs=2 if key in ("c2", "c5") else None)
