@@ -186,20 +186,21 @@ def test_autograd_glue():
     dY = synth.normal_bf16((4, 50, 136), 4)
     x = dev_bf16(X).requires_grad_(True)
     z = sl.linear_with_grad_accumulation(x, p1)
+    z.retain_grad()
     y = sl.linear_with_grad_accumulation(z, p2)
     y.backward(dev_bf16(dY))
     torch.cuda.synchronize()
     assert p1.grad is None and p2.grad is None
     assert p1.grad_added_to_main_grad and p2.grad_added_to_main_grad
-    Zr = ol.linear_fwd(X.reshape(200, 136), W1)
-    Zb = synth.f32_to_bf16_bits(host_f64(z).reshape(200, 264).astype(np.float32))   # what fc2 saw
-    assert ol.rel_err(host_f64(z).reshape(200, 264), Zr) <= TOL_BF16
+    Xm, dYm = X.reshape(200, 136), dY.reshape(200, 136)
+    Zb = host_bits(z).reshape(200, 264)           # what fc2 consumed (bf16)
+    dZb = host_bits(z.grad).reshape(200, 264)     # what fc1's backward consumed (bf16)
+    assert ol.rel_err(host_f64(z).reshape(200, 264), ol.linear_fwd(Xm, W1)) <= TOL_BF16
     assert ol.rel_err(host_f64(y).reshape(200, 136), ol.linear_fwd(Zb, W2)) <= TOL_BF16
-    dZ = ol.linear_dgrad(dY.reshape(200, 136), W2)
-    assert ol.rel_err(host_f64(buf.main_grad("fc2")), ol.linear_wgrad(Zb, dY.reshape(200, 136))) <= TOL_F32
-    dZb = host_f64(torch.autograd.grad(y, z, dev_bf16(dY), retain_graph=False)[0]) if False else None
-    assert dZb is None
-    assert ol.rel_err(host_f64(x.grad).reshape(200, 136), ol.linear_dgrad(dZ, W1)) <= 1e-2
+    assert ol.rel_err(host_f64(z.grad).reshape(200, 264), ol.linear_dgrad(dYm, W2)) <= TOL_BF16
+    assert ol.rel_err(host_f64(x.grad).reshape(200, 136), ol.linear_dgrad(dZb, W1)) <= TOL_BF16
+    assert ol.rel_err(host_f64(buf.main_grad("fc2")), ol.linear_wgrad(Zb, dYm)) <= TOL_F32
+    assert ol.rel_err(host_f64(buf.main_grad("fc1")), ol.linear_wgrad(Xm, dZb)) <= TOL_F32
 
 
 # ---------------------------------------------------------------------------------------------
