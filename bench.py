@@ -39,7 +39,22 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="time whole steps only (no per-launch events)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device copy of BYTES (reference for HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(nbytes: int) -> None:
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE counter readings
+    convert the counters of the GEMM kernels into HBM bytes."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
 
 
 def main():
@@ -48,6 +63,10 @@ def main():
         print("bench.py measures one GPU's shard only: run it with --gpus 1 (multi-GPU collectives "
               "are not part of this build)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch

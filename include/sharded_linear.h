@@ -102,10 +102,11 @@ int sl_linear_dgrad(void* stream, const void* dY, const void* W, void* dX,
  * [out, in] extent, so neighbouring views and padding of grad_data are untouched.
  *
  * workspace: device memory of at least sl_wgrad_workspace_bytes(T, in, out) bytes (may be 0, in
- * which case workspace may be NULL).  It holds split-K partial tiles and per-tile arrival
- * counters.  The counters must be zero before the workspace is first used (sl_grad_buffer_zero
- * on the whole workspace, or zero-filled allocation); every call leaves them zero again.  Calls
- * that may run concurrently must use distinct workspaces.
+ * which case workspace may be NULL).  Its first 64 KiB are per-tile arrival counters, the rest
+ * split-K partial tiles.  The counters must be zero before the workspace is first used
+ * (sl_grad_buffer_zero over the workspace, or a zero-filled allocation); every call leaves them
+ * zero again, so one workspace serves later calls of any shape that fit in it.  Calls that may
+ * run concurrently must use distinct workspaces.
  * ------------------------------------------------------------------------------------------- */
 size_t sl_wgrad_workspace_bytes(int64_t T, int64_t in, int64_t out);
 int sl_linear_wgrad_accum(void* stream, const void* X, const void* dY, float* main_grad,

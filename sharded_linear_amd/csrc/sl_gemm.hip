@@ -414,6 +414,9 @@ Shape pick_shape(int64_t M, int64_t N) {
   return {128, 128};
 }
 
+constexpr int64_t kCounters = 16384;      // arrival counters at the front of a wgrad workspace
+constexpr int64_t kCounterBytes = kCounters * 4;
+
 // Split count for the weight gradient: fill ~256 CUs with output tiles, keep >= 8 k stages per
 // split.
 void pick_splits(int64_t M, int64_t N, int64_t K, Shape sh, int* splits, int* kps) {
@@ -423,13 +426,16 @@ void pick_splits(int64_t M, int64_t N, int64_t K, Shape sh, int* splits, int* kp
   if (tiles < 200) s = (256 + tiles / 2) / tiles;
   if (s > nkt / 8) s = nkt / 8;
   if (s > 16) s = 16;
-  if (s < 1) s = 1;
+  if (s < 1 || tiles > kCounters) s = 1;
   int64_t per = (nkt + s - 1) / s;
   if (per < 1) per = 1;
   *kps = int(per);
   *splits = int(nkt == 0 ? 1 : (nkt + per - 1) / per);
 }
 
+// Workspace = [kCounters arrival counters][split-K partial tiles].  The counters sit at a fixed
+// offset for every shape, so one workspace serves calls of any shape: a call only ever touches
+// counters [0, tiles) and leaves them zero.
 size_t wgrad_ws_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   const Shape sh = pick_shape(M, N);
@@ -437,9 +443,7 @@ size_t wgrad_ws_bytes(int64_t M, int64_t N, int64_t K) {
   pick_splits(M, N, K, sh, &splits, &kps);
   if (splits <= 1) return 0;
   const int64_t tiles = ((M + sh.bm - 1) / sh.bm) * ((N + sh.bn - 1) / sh.bn);
-  const int64_t part = tiles * splits * int64_t(sh.bm) * sh.bn * 4;
-  const int64_t cnt = ((tiles * 4 + 255) / 256) * 256;
-  return size_t(part + cnt);
+  return size_t(kCounterBytes + tiles * splits * int64_t(sh.bm) * sh.bn * 4);
 }
 
 template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, Elem EA, Elem EB, Epi EPI>
@@ -467,9 +471,8 @@ int wgrad_setup(Args& a, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_by
   if (splits > 1) {
     const size_t need = wgrad_ws_bytes(M, N, K);
     if (!ws || ws_bytes < need || !aligned16(ws)) return SL_EWORKSPACE;
-    const int64_t tiles = ((M + sh.bm - 1) / sh.bm) * ((N + sh.bn - 1) / sh.bn);
-    a.ws = static_cast<float*>(ws);
-    a.cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + tiles * splits * int64_t(sh.bm) * sh.bn * 4);
+    a.cnt = static_cast<unsigned*>(ws);
+    a.ws = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
   }
   return SL_OK;
 }

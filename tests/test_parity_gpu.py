@@ -151,6 +151,24 @@ def test_neighbours_and_padding_untouched():
     assert ol.rel_err(host_f64(buf.main_grad("b")), want) <= TOL_F32
 
 
+def test_workspace_reused_across_shapes():
+    """One workspace serves split-K calls of different shapes in any order."""
+    say("case workspace reuse")
+    cases = [(4104, 264, 520), (1000, 2056, 264), (4100, 288, 3336), (4104, 264, 520)]
+    need = max(sl.sl_wgrad_workspace_bytes(*c) for c in cases)
+    assert all(sl.sl_wgrad_workspace_bytes(*c) > 0 for c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for T, n_in, n_out in cases:
+        X, W, dY = rand_case(T, n_in, n_out, 77)
+        G = torch.zeros((n_out, n_in), device="cuda")
+        sl.sl_linear_wgrad_accum(dev_bf16(X), dev_bf16(dY), G, workspace=ws)
+        torch.cuda.synchronize()
+        e = ol.rel_err(host_f64(G), ol.linear_wgrad(X, dY))
+        say(f"  T={T} in={n_in} out={n_out} rel err {e:.2e}")
+        assert e <= TOL_F32
+    assert int(torch.count_nonzero(ws[:65536])) == 0        # counters left zero
+
+
 def test_wgrad_is_deterministic():
     say("case determinism")
     X, W, dY = rand_case(8192, 1024, 2048, 11)   # split-K path at a C3-like shape
