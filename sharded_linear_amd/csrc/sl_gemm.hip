@@ -28,8 +28,11 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "sharded_linear.h"
+#include "sl_gemm2.h"
 
 namespace {
 
@@ -402,48 +405,88 @@ int check_dims(int64_t T, int64_t in, int64_t out, int64_t mult) {
   return SL_OK;
 }
 
-// One tile configuration per launch shape.  256x256 with 4 waves (each a 128x128 wave tile of
-// 16 MFMA blocks) when the grid fills the chip; 128x128 otherwise.
-struct Shape {
-  int bm, bn;
+// ---- launch planning ------------------------------------------------------------------------
+// bf16 operands go through the direct-to-LDS kernels (sl_gemm2.hip) whenever every operand's
+// byte extent fits their 31-bit buffer offsets; MXFP8 operands (dequantised on the way into
+// LDS) and larger operands use the register-staged kernels above.
+
+enum class Kind { Fwd, Dgrad, Wgrad };
+
+struct Plan {
+  bool v2;          // direct-to-LDS kernel family
+  int cfg;          // its tile configuration
+  int bm, bn, bk;   // macro-tile
+  int splits, kps;  // split-K (weight gradient only)
 };
 
-Shape pick_shape(int64_t M, int64_t N) {
-  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= 200) return {256, 256};
-  return {128, 128};
-}
-
+constexpr int64_t kMaxDmaBytes = 0x7FFFFFF0LL - 16;
 constexpr int64_t kCounters = 16384;      // arrival counters at the front of a wgrad workspace
 constexpr int64_t kCounterBytes = kCounters * 4;
 
-// Split count for the weight gradient: fill ~256 CUs with output tiles, keep >= 8 k stages per
-// split.
-void pick_splits(int64_t M, int64_t N, int64_t K, Shape sh, int* splits, int* kps) {
-  const int64_t tiles = ((M + sh.bm - 1) / sh.bm) * ((N + sh.bn - 1) / sh.bn);
-  const int64_t nkt = (K + kBK - 1) / kBK;
+int64_t ntiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
+
+// Tile configuration override for tuning: SL_GEMM_CONFIG="<n>" for every GEMM, or
+// "fwd=<n>,dgrad=<n>,wgrad=<n>" per GEMM; -1 (or unset) keeps the built-in choice.
+int config_override(Kind k) {
+  const char* e = getenv("SL_GEMM_CONFIG");
+  if (!e || !*e) return -1;
+  const char* key = k == Kind::Fwd ? "fwd=" : k == Kind::Dgrad ? "dgrad=" : "wgrad=";
+  const char* p = strstr(e, key);
+  int v = -1;
+  if (p) v = atoi(p + strlen(key));
+  else if (!strchr(e, '=')) v = atoi(e);
+  return (v >= 0 && v < kGemm2Configs) ? v : -1;
+}
+
+Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a_bytes, int64_t b_bytes) {
+  Plan p{};
+  p.v2 = !mxfp8 && a_bytes <= kMaxDmaBytes && b_bytes <= kMaxDmaBytes;
+  if (p.v2) {
+    int cfg = config_override(kind);
+    if (cfg < 0) {
+      if (ntiles(M, N, 256, 256) >= 240) cfg = 0;
+      else if (ntiles(M, N, 256, 128) >= 240) cfg = M >= N ? 3 : 4;
+      else cfg = 2;
+    }
+    p.cfg = cfg;
+    gemm2_tile(cfg, &p.bm, &p.bn);
+    p.bk = cfg == 0 ? 32 : 64;
+  } else {
+    const bool big = ntiles(M, N, 256, 256) >= 200;
+    p.bm = p.bn = big ? 256 : 128;
+    p.bk = kBK;
+  }
+  // split-K for the weight gradient: fill ~256 CUs with output tiles, keep >= 8 k stages per split
+  const int64_t tiles = ntiles(M, N, p.bm, p.bn);
+  const int64_t nkt = (K + p.bk - 1) / p.bk;
   int64_t s = 1;
-  if (tiles < 200) s = (256 + tiles / 2) / tiles;
-  if (s > nkt / 8) s = nkt / 8;
+  if (kind == Kind::Wgrad && tiles < 200) s = (256 + tiles / 2) / tiles;
+  const int64_t min_stages = p.bk == 32 ? 16 : 8;
+  if (s > nkt / min_stages) s = nkt / min_stages;
   if (s > 16) s = 16;
   if (s < 1 || tiles > kCounters) s = 1;
   int64_t per = (nkt + s - 1) / s;
   if (per < 1) per = 1;
-  *kps = int(per);
-  *splits = int(nkt == 0 ? 1 : (nkt + per - 1) / per);
+  p.kps = int(per);
+  p.splits = int(nkt == 0 ? 1 : (nkt + per - 1) / per);
+  return p;
 }
 
 // Workspace = [kCounters arrival counters][split-K partial tiles].  The counters sit at a fixed
 // offset for every shape, so one workspace serves calls of any shape: a call only ever touches
 // counters [0, tiles) and leaves them zero.
-size_t wgrad_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || N <= 0 || K <= 0) return 0;
-  const Shape sh = pick_shape(M, N);
-  int splits, kps;
-  pick_splits(M, N, K, sh, &splits, &kps);
-  if (splits <= 1) return 0;
-  const int64_t tiles = ((M + sh.bm - 1) / sh.bm) * ((N + sh.bn - 1) / sh.bn);
-  return size_t(kCounterBytes + tiles * splits * int64_t(sh.bm) * sh.bn * 4);
+size_t plan_ws_bytes(const Plan& p, int64_t M, int64_t N) {
+  if (p.splits <= 1) return 0;
+  return size_t(kCounterBytes + ntiles(M, N, p.bm, p.bn) * p.splits * int64_t(p.bm) * p.bn * 4);
+}
+
+// weight-gradient GEMM: M = out, N = in, K = T; A = dY [T, out], B = X [T, in] (bf16 or MXFP8)
+size_t wgrad_ws_bytes(int64_t T, int64_t in, int64_t out) {
+  if (T <= 0 || in <= 0 || out <= 0) return 0;
+  const Plan pb = make_plan(Kind::Wgrad, false, out, in, T, T * out * 2, T * in * 2);
+  const Plan pq = make_plan(Kind::Wgrad, true, out, in, T, T * out * 2, T * in);
+  const size_t a = plan_ws_bytes(pb, out, in), b = plan_ws_bytes(pq, out, in);
+  return a > b ? a : b;
 }
 
 template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, Elem EA, Elem EB, Epi EPI>
@@ -456,32 +499,40 @@ int launch(hipStream_t st, Args& a) {
 }
 
 template <bool A_KMAJ, bool B_KMAJ, Elem EA, Elem EB, Epi EPI>
-int run(hipStream_t st, Args& a) {
-  const Shape sh = pick_shape(a.M, a.N);
-  if (sh.bm == 256) return launch<256, 256, A_KMAJ, B_KMAJ, EA, EB, EPI>(st, a);
+int run_v1(hipStream_t st, Args& a, const Plan& p) {
+  if (p.bm == 256) return launch<256, 256, A_KMAJ, B_KMAJ, EA, EB, EPI>(st, a);
   return launch<128, 128, A_KMAJ, B_KMAJ, EA, EB, EPI>(st, a);
 }
 
-int wgrad_setup(Args& a, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes) {
-  const Shape sh = pick_shape(M, N);
-  int splits, kps;
-  pick_splits(M, N, K, sh, &splits, &kps);
-  a.splits = splits;
-  a.kt_per_split = kps;
-  if (splits > 1) {
-    const size_t need = wgrad_ws_bytes(M, N, K);
-    if (!ws || ws_bytes < need || !aligned16(ws)) return SL_EWORKSPACE;
+int run_v2(hipStream_t st, Kind kind, const Args& a, const Plan& p, int64_t a_bytes, int64_t b_bytes) {
+  Gemm2Args g{};
+  g.a = a.a.p; g.b = a.b.p; g.c = a.c;
+  g.lda = a.a.ld; g.ldb = a.b.ld; g.ldc = a.ldc;
+  g.a_bytes = uint32_t(a_bytes); g.b_bytes = uint32_t(b_bytes);
+  g.M = a.M; g.N = a.N; g.K = a.K;
+  g.splits = a.splits; g.kt_per_split = a.kt_per_split;
+  g.ws = a.ws; g.cnt = a.cnt;
+  g.cfg = p.cfg;
+  const int r = kind == Kind::Fwd ? gemm2_fwd(st, g) : kind == Kind::Dgrad ? gemm2_dgrad(st, g) : gemm2_wgrad(st, g);
+  return r == 0 ? SL_OK : SL_EHIP;
+}
+
+int bind_workspace(Args& a, const Plan& p, int64_t M, int64_t N, void* ws, size_t ws_bytes) {
+  a.splits = p.splits;
+  a.kt_per_split = p.kps;
+  if (p.splits > 1) {
+    if (!ws || ws_bytes < plan_ws_bytes(p, M, N) || !aligned16(ws)) return SL_EWORKSPACE;
     a.cnt = static_cast<unsigned*>(ws);
     a.ws = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
   }
   return SL_OK;
 }
 
-Args base_args(int64_t M, int64_t N, int64_t K) {
+Args base_args(int64_t M, int64_t N, int64_t K, const Plan& p) {
   Args a{};
   a.M = int(M); a.N = int(N); a.K = int(K);
   a.splits = 1;
-  a.kt_per_split = int((K + kBK - 1) / kBK);
+  a.kt_per_split = int((K + p.bk - 1) / p.bk);
   return a;
 }
 
@@ -509,12 +560,15 @@ extern "C" int sl_linear_fwd(void* stream, const void* X, const void* W, void* Y
   if (T == 0 || out == 0) return SL_OK;
   if (!Y || (in > 0 && (!X || !W))) return SL_EINVAL;
   if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return SL_EALIGN;
-  Args a = base_args(T, out, in);
+  const Plan p = make_plan(Kind::Fwd, false, T, out, in, T * in * 2, out * in * 2);
+  Args a = base_args(T, out, in, p);
   a.a = {X, nullptr, in, int(T)};
   a.b = {W, nullptr, in, int(out)};
   a.c = Y;
   a.ldc = out;
-  return run<true, true, Elem::BF16, Elem::BF16, Epi::StoreBF16>(static_cast<hipStream_t>(stream), a);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (p.v2) return run_v2(hs, Kind::Fwd, a, p, T * in * 2, out * in * 2);
+  return run_v1<true, true, Elem::BF16, Elem::BF16, Epi::StoreBF16>(hs, a, p);
 }
 
 extern "C" int sl_linear_dgrad(void* stream, const void* dY, const void* W, void* dX, int64_t T, int64_t in,
@@ -524,17 +578,20 @@ extern "C" int sl_linear_dgrad(void* stream, const void* dY, const void* W, void
   if (T == 0 || in == 0) return SL_OK;
   if (!dX || (out > 0 && (!dY || !W))) return SL_EINVAL;
   if (!aligned16(dY) || !aligned16(W) || !aligned16(dX)) return SL_EALIGN;
-  Args a = base_args(T, in, out);
+  const Plan p = make_plan(Kind::Dgrad, false, T, in, out, T * out * 2, out * in * 2);
+  Args a = base_args(T, in, out, p);
   a.a = {dY, nullptr, out, int(T)};
   a.b = {W, nullptr, in, int(in)};
   a.c = dX;
   a.ldc = in;
-  return run<true, false, Elem::BF16, Elem::BF16, Epi::StoreBF16>(static_cast<hipStream_t>(stream), a);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (p.v2) return run_v2(hs, Kind::Dgrad, a, p, T * out * 2, out * in * 2);
+  return run_v1<true, false, Elem::BF16, Elem::BF16, Epi::StoreBF16>(hs, a, p);
 }
 
 extern "C" size_t sl_wgrad_workspace_bytes(int64_t T, int64_t in, int64_t out) {
   if (T < 0 || in < 0 || out < 0) return 0;
-  return wgrad_ws_bytes(out, in, T);
+  return wgrad_ws_bytes(T, in, out);
 }
 
 extern "C" int sl_linear_wgrad_accum(void* stream, const void* X, const void* dY, float* main_grad, int64_t T,
@@ -544,14 +601,17 @@ extern "C" int sl_linear_wgrad_accum(void* stream, const void* X, const void* dY
   if (T == 0 || in == 0 || out == 0) return SL_OK;
   if (!X || !dY || !main_grad) return SL_EINVAL;
   if (!aligned16(X) || !aligned16(dY) || !aligned16(main_grad)) return SL_EALIGN;
-  Args a = base_args(out, in, T);
+  const Plan p = make_plan(Kind::Wgrad, false, out, in, T, T * out * 2, T * in * 2);
+  Args a = base_args(out, in, T, p);
   a.a = {dY, nullptr, out, int(out)};
   a.b = {X, nullptr, in, int(in)};
   a.c = main_grad;
   a.ldc = in;
-  st = wgrad_setup(a, out, in, T, workspace, workspace_bytes);
+  st = bind_workspace(a, p, out, in, workspace, workspace_bytes);
   if (st) return st;
-  return run<false, false, Elem::BF16, Elem::BF16, Epi::AccumF32>(static_cast<hipStream_t>(stream), a);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (p.v2) return run_v2(hs, Kind::Wgrad, a, p, T * out * 2, T * in * 2);
+  return run_v1<false, false, Elem::BF16, Elem::BF16, Epi::AccumF32>(hs, a, p);
 }
 
 extern "C" int sl_linear_fwd_mxfp8(void* stream, const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
@@ -562,12 +622,13 @@ extern "C" int sl_linear_fwd_mxfp8(void* stream, const uint8_t* Xq, const uint8_
   if (T == 0 || out == 0) return SL_OK;
   if (!Y || (in > 0 && (!Xq || !Xs || !Wq || !Ws))) return SL_EINVAL;
   if (!aligned16(Xq) || !aligned16(Wq) || !aligned16(Y)) return SL_EALIGN;
-  Args a = base_args(T, out, in);
+  const Plan p = make_plan(Kind::Fwd, true, T, out, in, T * in, out * in);
+  Args a = base_args(T, out, in, p);
   a.a = {Xq, Xs, in, int(T)};
   a.b = {Wq, Ws, in, int(out)};
   a.c = Y;
   a.ldc = out;
-  return run<true, true, Elem::MXFP8, Elem::MXFP8, Epi::StoreBF16>(static_cast<hipStream_t>(stream), a);
+  return run_v1<true, true, Elem::MXFP8, Elem::MXFP8, Epi::StoreBF16>(static_cast<hipStream_t>(stream), a, p);
 }
 
 extern "C" int sl_linear_dgrad_mxfp8w(void* stream, const void* dY, const uint8_t* Wq, const uint8_t* Ws,
@@ -578,12 +639,13 @@ extern "C" int sl_linear_dgrad_mxfp8w(void* stream, const void* dY, const uint8_
   if (T == 0 || in == 0) return SL_OK;
   if (!dX || (out > 0 && (!dY || !Wq || !Ws))) return SL_EINVAL;
   if (!aligned16(dY) || !aligned16(Wq) || !aligned16(dX)) return SL_EALIGN;
-  Args a = base_args(T, in, out);
+  const Plan p = make_plan(Kind::Dgrad, true, T, in, out, T * out * 2, out * in);
+  Args a = base_args(T, in, out, p);
   a.a = {dY, nullptr, out, int(T)};
   a.b = {Wq, Ws, in, int(in)};
   a.c = dX;
   a.ldc = in;
-  return run<true, false, Elem::BF16, Elem::MXFP8, Epi::StoreBF16>(static_cast<hipStream_t>(stream), a);
+  return run_v1<true, false, Elem::BF16, Elem::MXFP8, Epi::StoreBF16>(static_cast<hipStream_t>(stream), a, p);
 }
 
 extern "C" int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, const uint8_t* Xs, const void* dY,
@@ -595,12 +657,13 @@ extern "C" int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, con
   if (T == 0 || in == 0 || out == 0) return SL_OK;
   if (!Xq || !Xs || !dY || !main_grad) return SL_EINVAL;
   if (!aligned16(Xq) || !aligned16(dY) || !aligned16(main_grad)) return SL_EALIGN;
-  Args a = base_args(out, in, T);
+  const Plan p = make_plan(Kind::Wgrad, true, out, in, T, T * out * 2, T * in);
+  Args a = base_args(out, in, T, p);
   a.a = {dY, nullptr, out, int(out)};
   a.b = {Xq, Xs, in, int(in)};
   a.c = main_grad;
   a.ldc = in;
-  st = wgrad_setup(a, out, in, T, workspace, workspace_bytes);
+  st = bind_workspace(a, p, out, in, workspace, workspace_bytes);
   if (st) return st;
-  return run<false, false, Elem::BF16, Elem::MXFP8, Epi::AccumF32>(static_cast<hipStream_t>(stream), a);
+  return run_v1<false, false, Elem::BF16, Elem::MXFP8, Epi::AccumF32>(static_cast<hipStream_t>(stream), a, p);
 }

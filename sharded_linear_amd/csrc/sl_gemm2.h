@@ -1,0 +1,30 @@
+// Internal interface of the direct-to-LDS bf16 GEMM kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+struct Gemm2Args {
+  const void* a;        // A operand storage (bf16)
+  const void* b;        // B operand storage (bf16)
+  void* c;              // bf16 output, or fp32 main_grad for the accumulating kernel
+  int64_t lda, ldb, ldc;
+  uint32_t a_bytes, b_bytes;   // operand extents: loads past them return zeros
+  int M, N, K;
+  int tiles_m, tiles_n;
+  int splits, kt_per_split;
+  float* ws;            // split-K partial tiles (accumulating kernel)
+  unsigned* cnt;        // split-K arrival counters
+  int cfg;              // tile configuration, see gemm2_tile()
+};
+
+constexpr int kGemm2Configs = 5;
+
+// A K-major (k contiguous) and B K-major: forward.
+int gemm2_fwd(hipStream_t st, Gemm2Args g);
+// A K-major, B MN-major: dgrad.
+int gemm2_dgrad(hipStream_t st, Gemm2Args g);
+// A and B MN-major, fp32 accumulate into C: wgrad.
+int gemm2_wgrad(hipStream_t st, Gemm2Args g);
+// Macro-tile of configuration cfg.
+void gemm2_tile(int cfg, int* bm, int* bn);

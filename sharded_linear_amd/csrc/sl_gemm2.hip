@@ -1,0 +1,348 @@
+// bf16 GEMM core of the linear step with direct HBM->LDS operand staging (gfx950).
+//
+// Same three products as the register-staged kernels (forward, dgrad, fused wgrad-accumulate),
+// C[m][n] (+)= sum_k A(m,k) B(n,k), but operands travel from HBM straight into LDS with
+// buffer_load_dwordx4 ... lds: lane i of a wave writes 16 bytes at LDS base + 16 i, and lanes
+// whose element lies outside the matrix are given an out-of-range offset, so the hardware
+// writes zeros there.  A ring of S LDS stages keeps S-1 stages of loads in flight.
+//
+//  * K-major operand (k contiguous in HBM): LDS rows of BK k values, 16-byte chunks XOR-swizzled
+//    by row; MFMA fragments are read with ds_read_b128.
+//  * MN-major operand (m or n contiguous in HBM): LDS keeps the HBM orientation, rows of R free
+//    indices per k; MFMA fragments are read with ds_read_b64_tr_b16, which transposes 4x4 blocks
+//    of 16-bit values across each group of 16 lanes: result lane 4q+e, element j comes from
+//    source lane 4j+q, element e.  Source lane 4j+q reads 4 consecutive free indices at k row
+//    kb+j, so every result lane holds 4 consecutive k of one free index -- the MFMA layout.
+//
+// MFMA: v_mfma_f32_32x32x16_bf16 (lane l: row/column l%32, k = 8*(l/32)+0..7; result lane l
+// holds column l%32, rows 8*(r/4) + 4*(l/32) + r%4).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sl_gemm2.h"
+
+namespace sl2 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kXCD = 8;
+constexpr uint32_t kOOB = 0x7FFFFFF0u;        // offset past every operand extent: loads return zeros
+constexpr int kRsrcWord3 = 0x00020000;        // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int per = n / kXCD, rem = n % kXCD, x = b % kXCD;
+  return x * per + (x < rem ? x : rem) + b / kXCD;
+}
+
+// s_waitcnt with vmcnt <= N and the other counters unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Raw buffer descriptor over one operand (gfx9 layout: base, stride 0, num_records = byte
+// extent, format word).  Offsets outside the extent -- including kOOB, above every extent the
+// host admits -- read zeros instead of touching memory.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = int(uint32_t(a));
+  r[1] = int(uint32_t(a >> 32) & 0xFFFFu);
+  r[2] = int(bytes);
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+
+// One 16-byte-per-lane HBM->LDS load: lane i writes LDS [lds + 16 i, +16).  Issued as inline
+// assembly so that the compiler does not guard every later LDS read with a full vmcnt wait;
+// the kernel orders these loads itself with wait_vmcnt<>() and a barrier.
+__device__ __forceinline__ void lds_dma16(i32x4 rs, uint32_t lds, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rs), "{m0}"(lds) : "memory");
+}
+
+// ---- K-major operand: LDS [R rows][BK] bf16 -----------------------------------------------
+template <int R, int BK>
+struct KMaj {
+  static constexpr int kRowBytes = BK * 2;
+  static constexpr int kCPR = BK / 8;                  // 16-byte chunks per row
+  static constexpr int kRowsPer128 = 128 / kRowBytes;  // rows sharing one 128-byte bank window
+  static constexpr int kBytes = R * kRowBytes;
+  static constexpr int kLoads = kBytes / 1024;         // wave-loads of 1 KiB per stage
+  __device__ static __forceinline__ int swz(int r) { return (r / kRowsPer128) % kCPR; }
+
+  // Wave `w` issues loads wl = w, w + waves, ...; lane i fills LDS bytes [1024 wl + 16 i, +16).
+  template <int WAVES>
+  __device__ static __forceinline__ void load(i32x4 rs, char* lds, int lane, int wave,
+                                              int row0, int rows, int k0, int K, int64_t ld) {
+#pragma unroll
+    for (int it = 0; it < kLoads / WAVES; ++it) {
+      const int wl = it * WAVES + wave;
+      const int p = wl * 64 + lane;                      // 16-byte slot
+      const int r = p / kCPR, c = (p % kCPR) ^ swz(p / kCPR);
+      const int gr = row0 + r, k = k0 + c * 8;
+      const uint32_t off = (gr < rows && k < K) ? uint32_t((int64_t(gr) * ld + k) * 2) : kOOB;
+      lds_dma16(rs, lds_addr(lds + wl * 1024), off);
+    }
+  }
+  // fragment of 32 rows starting at r0, k16 step ks: lane l gets row r0 + l%32, k 8(l/32)..+7
+  __device__ static __forceinline__ bf16x8 frag(const char* lds, int r0, int ks, int lane) {
+    const int r = r0 + (lane & 31);
+    const int c = ks * 2 + (lane >> 5);
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + r * kRowBytes + ((c ^ swz(r)) << 4));
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+// ---- MN-major operand: LDS [BK rows (k)][R] bf16 -------------------------------------------
+template <int R, int BK>
+struct MNMaj {
+  static constexpr int kRowBytes = R * 2;
+  static constexpr int kCPR = R / 8;
+  static constexpr int kBytes = BK * kRowBytes;
+  static constexpr int kLoads = kBytes / 1024;
+  static_assert(kRowBytes % 128 == 0, "rows must span whole bank windows");
+  __device__ static __forceinline__ int swz(int k) { return 2 * (k & 3); }
+
+  template <int WAVES>
+  __device__ static __forceinline__ void load(i32x4 rs, char* lds, int lane, int wave,
+                                              int col0, int cols, int k0, int K, int64_t ld) {
+#pragma unroll
+    for (int it = 0; it < kLoads / WAVES; ++it) {
+      const int wl = it * WAVES + wave;
+      const int p = wl * 64 + lane;
+      const int k = p / kCPR, c = (p % kCPR) ^ swz(p / kCPR);
+      const int gk = k0 + k, gc = col0 + c * 8;
+      const uint32_t off = (gk < K && gc < cols) ? uint32_t((int64_t(gk) * ld + gc) * 2) : kOOB;
+      lds_dma16(rs, lds_addr(lds + wl * 1024), off);
+    }
+  }
+  // fragment of 32 free indices from f0, k16 step ks, via two transposing reads
+  __device__ static __forceinline__ bf16x8 frag(const char* lds, int f0, int ks, int lane) {
+    const int g = lane >> 4, s = lane & 15, j = s >> 2, q = s & 3;
+    const int f = f0 + 16 * (g & 1) + 4 * q;
+    const int k = ks * 16 + 8 * (g >> 1) + j;
+    const int cb = f >> 3, eb = (f & 7) << 1;
+    const char* p0 = lds + k * kRowBytes + ((cb ^ swz(k)) << 4) + eb;
+    const char* p1 = lds + (k + 4) * kRowBytes + ((cb ^ swz(k + 4)) << 4) + eb;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
+    const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+template <bool KM, int R, int BK>
+struct OpSel { using T = KMaj<R, BK>; };
+template <int R, int BK>
+struct OpSel<false, R, BK> { using T = MNMaj<R, BK>; };
+
+template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC>
+__global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
+  constexpr int WAVES = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
+  using OA = typename OpSel<A_KM, BM, BK>::T;
+  using OB = typename OpSel<B_KM, BN, BK>::T;
+  constexpr int kStage = OA::kBytes + OB::kBytes;
+  constexpr int kLoadsPerThread = (OA::kLoads + OB::kLoads) / WAVES;
+  static_assert(OA::kLoads % WAVES == 0 && OB::kLoads % WAVES == 0, "loads per wave");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int t = xcd_remap(blockIdx.x, ntiles);
+  const int group = t / (8 * g.tiles_n);
+  const int first_m = group * 8;
+  const int gsz = min(g.tiles_m - first_m, 8);
+  const int tm = first_m + (t % (8 * g.tiles_n)) % gsz;
+  const int tn = (t % (8 * g.tiles_n)) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int split = blockIdx.z;
+  const int nkt = (g.K + BK - 1) / BK;
+  const int kt0 = split * g.kt_per_split;
+  const int kt1 = min(nkt, kt0 + g.kt_per_split);
+  const int nk = kt1 - kt0;
+
+  const i32x4 ra = rsrc(g.a, g.a_bytes), rb = rsrc(g.b, g.b_bytes);
+
+  auto issue = [&](int kt, int slot) {
+    char* base = smem + slot * kStage;
+    const int k0 = kt * BK;
+    OA::template load<WAVES>(ra, base, lane, wave, m0, g.M, k0, g.K, g.lda);
+    OB::template load<WAVES>(rb, base + OA::kBytes, lane, wave, n0, g.N, k0, g.K, g.ldb);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // prologue: S-1 stages in flight (stages past the end load zeros: uniform wait counts)
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(kt0 + (s < nk ? s : nk), s);
+
+  for (int it = 0; it < nk; ++it) {
+    wait_vmcnt<(S - 2) * kLoadsPerThread>();
+    __syncthreads();
+    {
+      const int nxt = it + S - 1;
+      issue(kt0 + (nxt < nk ? nxt : nk), nxt % S);
+    }
+    const char* la = smem + (it % S) * kStage;
+    const char* lb = la + OA::kBytes;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[i] = OA::frag(la, wm * WM + i * 32, ks, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = OB::frag(lb, wn * WN + j * 32, ks, lane);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue ----------------------------------------------------------------------------
+  const int rib = 4 * (lane >> 5), cib = lane & 31;
+  if constexpr (!ACC) {
+    __bf16* C = static_cast<__bf16*>(g.c);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WN + j * 32 + cib;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + rib + (r & 3);
+          if (m < g.M && n < g.N) C[int64_t(m) * g.ldc + n] = static_cast<__bf16>(acc[i][j][r]);
+        }
+      }
+  } else {
+    float* C = static_cast<float*>(g.c);
+    constexpr int NT = WAVES * 64;
+    if (g.splits > 1) {
+      __shared__ int last_flag;
+      constexpr int V = TM * TN * 4;
+      const int tile = tm * g.tiles_n + tn;
+      float4* mine = reinterpret_cast<float4*>(g.ws) + (int64_t(tile) * g.splits + split) * V * NT;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            mine[((i * TN + j) * 4 + q) * NT + tid] =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      __threadfence();
+      __syncthreads();
+      if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(g.cnt + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = (prev == unsigned(g.splits - 1));
+      }
+      __syncthreads();
+      if (!last_flag) return;
+      __threadfence();
+      const float4* base = reinterpret_cast<const float4*>(g.ws) + int64_t(tile) * g.splits * V * NT;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int sp = 0; sp < g.splits; ++sp) {
+              float4 v;
+              if (sp == split)
+                v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+              else
+                v = base[(int64_t(sp) * V + (i * TN + j) * 4 + q) * NT + tid];
+              s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+            }
+            acc[i][j][4 * q] = s.x; acc[i][j][4 * q + 1] = s.y;
+            acc[i][j][4 * q + 2] = s.z; acc[i][j][4 * q + 3] = s.w;
+          }
+      if (tid == 0) __hip_atomic_store(g.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WN + j * 32 + cib;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + rib + (r & 3);
+          if (m < g.M && n < g.N) {
+            float* p = C + int64_t(m) * g.ldc + n;
+            *p = *p + acc[i][j][r];
+          }
+        }
+      }
+  }
+}
+
+template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC>
+int launch_cfg(hipStream_t st, Gemm2Args g) {
+  using OA = typename OpSel<A_KM, BM, BK>::T;
+  using OB = typename OpSel<B_KM, BN, BK>::T;
+  constexpr int lds = S * (OA::kBytes + OB::kBytes);
+  auto kfn = gemm2<BM, BN, BK, S, WGM, WGN, A_KM, B_KM, ACC>;
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+      return -5;
+    attr = true;
+  }
+  g.tiles_m = (g.M + BM - 1) / BM;
+  g.tiles_n = (g.N + BN - 1) / BN;
+  hipLaunchKernelGGL(kfn, dim3(g.tiles_m * g.tiles_n, 1, g.splits), dim3(WGM * WGN * 64), lds, st, g);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+}  // namespace sl2
+
+// ---- dispatch ------------------------------------------------------------------------------
+// Tile configurations, indexed by Gemm2Args::cfg:
+//   0: 256x256, BK 32, 4 stages, 4 waves (128x128 wave tiles)    LDS 128 KiB
+//   1: 256x256, BK 64, 2 stages, 4 waves                          LDS 128 KiB
+//   2: 128x128, BK 64, 3 stages, 4 waves (64x64 wave tiles)       LDS  96 KiB
+//   3: 256x128, BK 64, 2 stages, 4 waves (128x64 wave tiles)      LDS  96 KiB
+//   4: 128x256, BK 64, 2 stages, 4 waves (64x128 wave tiles)      LDS  96 KiB
+#define SL2_DISPATCH(AK, BKM, ACC)                                                                 \
+  switch (g.cfg) {                                                                                 \
+    case 0: return sl2::launch_cfg<256, 256, 32, 4, 2, 2, AK, BKM, ACC>(st, g);                   \
+    case 1: return sl2::launch_cfg<256, 256, 64, 2, 2, 2, AK, BKM, ACC>(st, g);                   \
+    case 2: return sl2::launch_cfg<128, 128, 64, 3, 2, 2, AK, BKM, ACC>(st, g);                   \
+    case 3: return sl2::launch_cfg<256, 128, 64, 2, 2, 2, AK, BKM, ACC>(st, g);                   \
+    case 4: return sl2::launch_cfg<128, 256, 64, 2, 2, 2, AK, BKM, ACC>(st, g);                   \
+    default: return -1;                                                                            \
+  }
+
+int gemm2_fwd(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, true, false) }
+int gemm2_dgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, false, false) }
+int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) }
+
+void gemm2_tile(int cfg, int* bm, int* bn) {
+  static const int t[5][2] = {{256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}};
+  *bm = t[cfg][0];
+  *bn = t[cfg][1];
+}

@@ -64,6 +64,27 @@ def test_fwd_dgrad_wgrad_elementwise(T, n_in, n_out):
     assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
 
 
+@pytest.mark.parametrize("cfg", range(5))
+@pytest.mark.parametrize("T,n_in,n_out", [(300, 264, 520), (1000, 2056, 264), (2111, 1032, 776)])
+def test_every_tile_config(monkeypatch, cfg, T, n_in, n_out):
+    """Each direct-to-LDS tile configuration, forced through SL_GEMM_CONFIG, on ragged shapes."""
+    say(f"case cfg={cfg} T={T} in={n_in} out={n_out}")
+    monkeypatch.setenv("SL_GEMM_CONFIG", str(cfg))
+    X, W, dY = rand_case(T, n_in, n_out, 31 + cfg)
+    G0 = synth.normal_f32((n_out, n_in), 98)
+    Xd, Wd, dYd = dev_bf16(X), dev_bf16(W), dev_bf16(dY)
+    Gd = torch.from_numpy(G0).cuda()
+    Y = sl.sl_linear_fwd(Xd, Wd)
+    dX = sl.sl_linear_dgrad(dYd, Wd)
+    sl.sl_linear_wgrad_accum(Xd, dYd, Gd)
+    torch.cuda.synchronize()
+    e_y = ol.rel_err(host_f64(Y), ol.linear_fwd(X, W))
+    e_dx = ol.rel_err(host_f64(dX), ol.linear_dgrad(dY, W))
+    e_g = ol.rel_err(host_f64(Gd), ol.linear_wgrad_accum(G0, X, dY))
+    say(f"  rel err Y {e_y:.2e} dX {e_dx:.2e} main_grad {e_g:.2e}")
+    assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
+
+
 def test_c1_two_microbatches_into_buffer_view():
     w = configs.WORKLOADS["c1"]
     say("case c1")
