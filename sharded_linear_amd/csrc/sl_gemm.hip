@@ -327,42 +327,40 @@ gemm_kernel(Args args) {
       // publish this split's partial, then count arrivals; the last one reduces
       constexpr int V = TM * TN * 4;                     // float4 per thread
       const int tile = tm * args.tiles_n + tn;
-      float4* mine = reinterpret_cast<float4*>(args.ws) + (int64_t(tile) * args.splits + split) * V * NT;
+      // Partials travel through device-coherent (agent-scope) relaxed atomic stores and loads,
+      // which bypass the per-XCD L2 state; each thread drains its stores (vmcnt 0) before the
+      // barrier that precedes the arrival count, so the last arriver sees every partial.  No
+      // cache-wide writeback or invalidate is needed, and co-resident blocks keep their L2.
+      float* mine = args.ws + (int64_t(tile) * args.splits + split) * V * 4 * NT;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            mine[((i * TN + j) * 4 + q) * NT + tid] =
-                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-      __threadfence();
+          for (int r = 0; r < 16; ++r)
+            __hip_atomic_store(mine + ((i * TN + j) * 16 + r) * NT + tid, acc[i][j][r], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(args.cnt + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned prev = __hip_atomic_fetch_add(args.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last_flag = (prev == unsigned(args.splits - 1));
       }
       __syncthreads();
       if (!last_flag) return;
-      __threadfence();
-      const float4* base = reinterpret_cast<const float4*>(args.ws) + int64_t(tile) * args.splits * V * NT;
+      const float* base = args.ws + int64_t(tile) * args.splits * V * 4 * NT;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int sp = 0; sp < args.splits; ++sp) {
-              float4 v;
-              if (sp == split)
-                v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-              else
-                v = base[(int64_t(sp) * V + (i * TN + j) * 4 + q) * NT + tid];
-              s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-            }
-            acc[i][j][4 * q] = s.x; acc[i][j][4 * q + 1] = s.y;
-            acc[i][j][4 * q + 2] = s.z; acc[i][j][4 * q + 3] = s.w;
+          for (int r = 0; r < 16; ++r) {
+            float sum = 0.f;
+            for (int sp = 0; sp < args.splits; ++sp)
+              sum += sp == split ? acc[i][j][r]
+                                 : __hip_atomic_load(base + (int64_t(sp) * V * 4 + (i * TN + j) * 16 + r) * NT + tid,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            acc[i][j][r] = sum;
           }
       if (tid == 0) __hip_atomic_store(args.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -444,13 +442,13 @@ Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a
   if (p.v2) {
     int cfg = config_override(kind);
     if (cfg < 0) {
-      if (ntiles(M, N, 256, 256) >= 240) cfg = 0;
+      if (ntiles(M, N, 256, 256) >= 240) cfg = 1;
       else if (ntiles(M, N, 256, 128) >= 240) cfg = M >= N ? 3 : 4;
       else cfg = 2;
     }
     p.cfg = cfg;
     gemm2_tile(cfg, &p.bm, &p.bn);
-    p.bk = cfg == 0 ? 32 : 64;
+    p.bk = cfg == 0 ? 32 : 64;   // every other configuration stages 64 k per LDS slot
   } else {
     const bool big = ntiles(M, N, 256, 256) >= 200;
     p.bm = p.bn = big ? 256 : 128;

@@ -75,10 +75,16 @@ template <int R, int BK>
 struct KMaj {
   static constexpr int kRowBytes = BK * 2;
   static constexpr int kCPR = BK / 8;                  // 16-byte chunks per row
-  static constexpr int kRowsPer128 = 128 / kRowBytes;  // rows sharing one 128-byte bank window
   static constexpr int kBytes = R * kRowBytes;
   static constexpr int kLoads = kBytes / 1024;         // wave-loads of 1 KiB per stage
-  __device__ static __forceinline__ int swz(int r) { return (r / kRowsPer128) % kCPR; }
+  static_assert(BK == 32 || BK == 64, "row swizzles are defined for BK 32 and 64");
+  // XOR swizzle of 16-byte chunks: 8 consecutive rows (a 128-byte bank window per 8 lanes of a
+  // 32-bank LDS phase) and 16 consecutive rows (256 bytes per 16 lanes of a 64-bank phase)
+  // reading the same logical chunk all land on distinct banks.
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);
+    else return ((r >> 1) ^ (r >> 3)) & 3;
+  }
 
   // Wave `w` issues loads wl = w, w + waves, ...; lane i fills LDS bytes [1024 wl + 16 i, +16).
   template <int WAVES>
@@ -111,7 +117,10 @@ struct MNMaj {
   static constexpr int kBytes = BK * kRowBytes;
   static constexpr int kLoads = kBytes / 1024;
   static_assert(kRowBytes % 128 == 0, "rows must span whole bank windows");
-  __device__ static __forceinline__ int swz(int k) { return 2 * (k & 3); }
+  // XOR swizzle of 16-byte chunks by k row: for the 4 rows x 16 free indices read by each
+  // 16-lane group of ds_read_b64_tr_b16 (and the 4 x 32 read by 32 lanes), the 32-byte chunk
+  // pairs are pair ^ {0, 5, 2, 7}, distinct within 128- and 256-byte bank windows.
+  __device__ static __forceinline__ int swz(int k) { return ((k & 3) ^ ((k & 1) << 2)) << 1; }
 
   template <int WAVES>
   __device__ static __forceinline__ void load(i32x4 rs, char* lds, int lane, int wave,
@@ -244,42 +253,40 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
       __shared__ int last_flag;
       constexpr int V = TM * TN * 4;
       const int tile = tm * g.tiles_n + tn;
-      float4* mine = reinterpret_cast<float4*>(g.ws) + (int64_t(tile) * g.splits + split) * V * NT;
+      // Partials travel through device-coherent (agent-scope) relaxed atomic stores and loads,
+      // which bypass the per-XCD L2 state; each thread drains its stores (vmcnt 0) before the
+      // barrier that precedes the arrival count, so the last arriver sees every partial.  No
+      // cache-wide writeback or invalidate is needed, and co-resident blocks keep their L2.
+      float* mine = g.ws + (int64_t(tile) * g.splits + split) * V * 4 * NT;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            mine[((i * TN + j) * 4 + q) * NT + tid] =
-                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-      __threadfence();
+          for (int r = 0; r < 16; ++r)
+            __hip_atomic_store(mine + ((i * TN + j) * 16 + r) * NT + tid, acc[i][j][r], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(g.cnt + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned prev = __hip_atomic_fetch_add(g.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last_flag = (prev == unsigned(g.splits - 1));
       }
       __syncthreads();
       if (!last_flag) return;
-      __threadfence();
-      const float4* base = reinterpret_cast<const float4*>(g.ws) + int64_t(tile) * g.splits * V * NT;
+      const float* base = g.ws + int64_t(tile) * g.splits * V * 4 * NT;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int sp = 0; sp < g.splits; ++sp) {
-              float4 v;
-              if (sp == split)
-                v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-              else
-                v = base[(int64_t(sp) * V + (i * TN + j) * 4 + q) * NT + tid];
-              s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-            }
-            acc[i][j][4 * q] = s.x; acc[i][j][4 * q + 1] = s.y;
-            acc[i][j][4 * q + 2] = s.z; acc[i][j][4 * q + 3] = s.w;
+          for (int r = 0; r < 16; ++r) {
+            float sum = 0.f;
+            for (int sp = 0; sp < g.splits; ++sp)
+              sum += sp == split ? acc[i][j][r]
+                                 : __hip_atomic_load(base + (int64_t(sp) * V * 4 + (i * TN + j) * 16 + r) * NT + tid,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            acc[i][j][r] = sum;
           }
       if (tid == 0) __hip_atomic_store(g.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -327,6 +334,8 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
 //   2: 128x128, BK 64, 3 stages, 4 waves (64x64 wave tiles)       LDS  96 KiB
 //   3: 256x128, BK 64, 2 stages, 4 waves (128x64 wave tiles)      LDS  96 KiB
 //   4: 128x256, BK 64, 2 stages, 4 waves (64x128 wave tiles)      LDS  96 KiB
+//   5: 256x256, BK 64, 2 stages, 8 waves 2x4 (128x64 wave tiles)  LDS 128 KiB
+//   6: 256x256, BK 64, 2 stages, 8 waves 4x2 (64x128 wave tiles)  LDS 128 KiB
 #define SL2_DISPATCH(AK, BKM, ACC)                                                                 \
   switch (g.cfg) {                                                                                 \
     case 0: return sl2::launch_cfg<256, 256, 32, 4, 2, 2, AK, BKM, ACC>(st, g);                   \
@@ -334,6 +343,8 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
     case 2: return sl2::launch_cfg<128, 128, 64, 3, 2, 2, AK, BKM, ACC>(st, g);                   \
     case 3: return sl2::launch_cfg<256, 128, 64, 2, 2, 2, AK, BKM, ACC>(st, g);                   \
     case 4: return sl2::launch_cfg<128, 256, 64, 2, 2, 2, AK, BKM, ACC>(st, g);                   \
+    case 5: return sl2::launch_cfg<256, 256, 64, 2, 2, 4, AK, BKM, ACC>(st, g);                   \
+    case 6: return sl2::launch_cfg<256, 256, 64, 2, 4, 2, AK, BKM, ACC>(st, g);                   \
     default: return -1;                                                                            \
   }
 
@@ -342,7 +353,7 @@ int gemm2_dgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, false, false) 
 int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) }
 
 void gemm2_tile(int cfg, int* bm, int* bn) {
-  static const int t[5][2] = {{256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}};
+  static const int t[7][2] = {{256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256}, {256, 256}};
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }
