@@ -101,11 +101,10 @@ int sl_linear_dgrad(void* stream, const void* dY, const void* W, void* dX,
  * never rounded and never stored on its own; main_grad is read and written only inside its
  * [out, in] extent, so neighbouring views and padding of grad_data are untouched.
  *
- * workspace: device memory of at least sl_wgrad_workspace_bytes(T, in, out) bytes (may be 0, in
- * which case workspace may be NULL).  Its first 64 KiB are per-tile arrival counters, the rest
- * split-K partial tiles.  The counters must be zero before the workspace is first used
- * (sl_grad_buffer_zero over the workspace, or a zero-filled allocation); every call leaves them
- * zero again, so one workspace serves later calls of any shape that fit in it.  Calls that may
+ * workspace: device memory of at least sl_wgrad_workspace_bytes(T, in, out) bytes (0 when the
+ * shape needs no split-K; workspace may then be NULL).  It holds fp32 split-K partial planes
+ * [splits][out][in], written and then read within the call; its initial contents do not
+ * matter.  A split call launches a second, reducing kernel on the same stream.  Calls that may
  * run concurrently must use distinct workspaces.
  * ------------------------------------------------------------------------------------------- */
 size_t sl_wgrad_workspace_bytes(int64_t T, int64_t in, int64_t out);

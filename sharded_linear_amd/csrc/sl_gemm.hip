@@ -21,10 +21,10 @@
 // E4M3 data, one E8M0 scale per 32 elements) are dequantised exactly to bf16 as they are moved
 // into LDS, then take the same MFMA path.
 //
-// Split-K for the weight gradient is deterministic: every split writes its fp32 partial tile
-// to the workspace and bumps the tile's counter; the split that arrives last adds all partials
-// in split order and performs the single read-modify-write of main_grad, then re-arms the
-// counter.  No block ever waits on another, so every launch drains.
+// Split-K for the weight gradient is deterministic and needs no cross-block synchronisation:
+// each split writes its fp32 partial into its own plane of the workspace, and a second kernel
+// on the same stream adds the planes in split order and performs the single read-modify-write
+// of main_grad.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -60,8 +60,7 @@ struct Args {
   int M, N, K;
   int tiles_m, tiles_n;
   int splits, kt_per_split;
-  float* ws;            // split-K partial tiles
-  unsigned* cnt;        // split-K arrival counters, one per output tile
+  float* ws;            // split-K partial planes [splits][M][N]
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -229,7 +228,6 @@ gemm_kernel(Args args) {
 
   __shared__ uint4 lds_a[2][BM * kCH];
   __shared__ uint4 lds_b[2][BN * kCH];
-  __shared__ int last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -322,48 +320,11 @@ gemm_kernel(Args args) {
         }
       }
   } else {
-    float* C = static_cast<float*>(args.c);
-    if (args.splits > 1) {
-      // publish this split's partial, then count arrivals; the last one reduces
-      constexpr int V = TM * TN * 4;                     // float4 per thread
-      const int tile = tm * args.tiles_n + tn;
-      // Partials travel through device-coherent (agent-scope) relaxed atomic stores and loads,
-      // which bypass the per-XCD L2 state; each thread drains its stores (vmcnt 0) before the
-      // barrier that precedes the arrival count, so the last arriver sees every partial.  No
-      // cache-wide writeback or invalidate is needed, and co-resident blocks keep their L2.
-      float* mine = args.ws + (int64_t(tile) * args.splits + split) * V * 4 * NT;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            __hip_atomic_store(mine + ((i * TN + j) * 16 + r) * NT + tid, acc[i][j][r], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(args.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (prev == unsigned(args.splits - 1));
-      }
-      __syncthreads();
-      if (!last_flag) return;
-      const float* base = args.ws + int64_t(tile) * args.splits * V * 4 * NT;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float sum = 0.f;
-            for (int sp = 0; sp < args.splits; ++sp)
-              sum += sp == split ? acc[i][j][r]
-                                 : __hip_atomic_load(base + (int64_t(sp) * V * 4 + (i * TN + j) * 16 + r) * NT + tid,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            acc[i][j][r] = sum;
-          }
-      if (tid == 0) __hip_atomic_store(args.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // Unsplit: the single fp32 read-modify-write of main_grad.  Split-K: this split's partial
+    // goes to its own plane ws[split][M][N]; splitk_reduce adds the planes into main_grad.
+    const bool direct = args.splits == 1;
+    float* C = direct ? static_cast<float*>(args.c) : args.ws + int64_t(split) * args.M * args.N;
+    const int64_t ldc = direct ? args.ldc : args.N;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -373,11 +334,29 @@ gemm_kernel(Args args) {
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + row_in_blk + (r & 3);
           if (m < args.M && n < args.N) {
-            float* p = C + int64_t(m) * args.ldc + n;
-            *p = *p + acc[i][j][r];
+            float* p = C + int64_t(m) * ldc + n;
+            *p = direct ? *p + acc[i][j][r] : acc[i][j][r];
           }
         }
       }
+  }
+}
+
+// main_grad[m][n] += sum over splits s (in order) of ws[s][m][n]; n counted in float4 (N % 4 == 0).
+__global__ void splitk_reduce(float* C, int64_t ldc, const float* ws, int M, int N, int splits) {
+  const int64_t n4 = N / 4, total = int64_t(M) * n4, plane = int64_t(M) * n4;
+  const float4* w = reinterpret_cast<const float4*>(ws);
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < splits; ++sp) {
+      const float4 v = w[sp * plane + i];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    float4* p = reinterpret_cast<float4*>(C + (i / n4) * ldc) + (i % n4);
+    float4 c = *p;
+    c.x += s.x; c.y += s.y; c.z += s.z; c.w += s.w;
+    *p = c;
   }
 }
 
@@ -418,13 +397,12 @@ struct Plan {
 };
 
 constexpr int64_t kMaxDmaBytes = 0x7FFFFFF0LL - 16;
-constexpr int64_t kCounters = 16384;      // arrival counters at the front of a wgrad workspace
-constexpr int64_t kCounterBytes = kCounters * 4;
 
 int64_t ntiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
-// Tile configuration override for tuning: SL_GEMM_CONFIG="<n>" for every GEMM, or
-// "fwd=<n>,dgrad=<n>,wgrad=<n>" per GEMM; -1 (or unset) keeps the built-in choice.
+// Tuning overrides.  SL_GEMM_CONFIG="<n>" forces tile configuration n for every bf16 GEMM, or
+// "fwd=<n>,dgrad=<n>,wgrad=<n>" per GEMM; SL_SPLITK="<n>" forces the weight gradient's split
+// count.  Unset (or out of range) keeps the built-in choice.
 int config_override(Kind k) {
   const char* e = getenv("SL_GEMM_CONFIG");
   if (!e || !*e) return -1;
@@ -436,19 +414,24 @@ int config_override(Kind k) {
   return (v >= 0 && v < kGemm2Configs) ? v : -1;
 }
 
+int splits_override() {
+  const char* e = getenv("SL_SPLITK");
+  const int v = (e && *e) ? atoi(e) : 0;
+  return (v >= 1 && v <= 64) ? v : 0;
+}
+
 Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a_bytes, int64_t b_bytes) {
   Plan p{};
   p.v2 = !mxfp8 && a_bytes <= kMaxDmaBytes && b_bytes <= kMaxDmaBytes;
   if (p.v2) {
     int cfg = config_override(kind);
     if (cfg < 0) {
-      if (ntiles(M, N, 256, 256) >= 240) cfg = 1;
+      if (ntiles(M, N, 256, 256) >= 200 || kind == Kind::Wgrad) cfg = 5;
       else if (ntiles(M, N, 256, 128) >= 240) cfg = M >= N ? 3 : 4;
       else cfg = 2;
     }
     p.cfg = cfg;
-    gemm2_tile(cfg, &p.bm, &p.bn);
-    p.bk = cfg == 0 ? 32 : 64;   // every other configuration stages 64 k per LDS slot
+    gemm2_tile(cfg, &p.bm, &p.bn, &p.bk);
   } else {
     const bool big = ntiles(M, N, 256, 256) >= 200;
     p.bm = p.bn = big ? 256 : 128;
@@ -462,7 +445,8 @@ Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a
   const int64_t min_stages = p.bk == 32 ? 16 : 8;
   if (s > nkt / min_stages) s = nkt / min_stages;
   if (s > 16) s = 16;
-  if (s < 1 || tiles > kCounters) s = 1;
+  if (s < 1) s = 1;
+  if (kind == Kind::Wgrad && splits_override()) s = splits_override();
   int64_t per = (nkt + s - 1) / s;
   if (per < 1) per = 1;
   p.kps = int(per);
@@ -470,12 +454,11 @@ Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a
   return p;
 }
 
-// Workspace = [kCounters arrival counters][split-K partial tiles].  The counters sit at a fixed
-// offset for every shape, so one workspace serves calls of any shape: a call only ever touches
-// counters [0, tiles) and leaves them zero.
+// Workspace = split-K partial planes [splits][M][N] fp32; written before it is read within one
+// call, so its initial contents never matter.
 size_t plan_ws_bytes(const Plan& p, int64_t M, int64_t N) {
   if (p.splits <= 1) return 0;
-  return size_t(kCounterBytes + ntiles(M, N, p.bm, p.bn) * p.splits * int64_t(p.bm) * p.bn * 4);
+  return size_t(int64_t(p.splits) * M * N * 4);
 }
 
 // weight-gradient GEMM: M = out, N = in, K = T; A = dY [T, out], B = X [T, in] (bf16 or MXFP8)
@@ -509,7 +492,7 @@ int run_v2(hipStream_t st, Kind kind, const Args& a, const Plan& p, int64_t a_by
   g.a_bytes = uint32_t(a_bytes); g.b_bytes = uint32_t(b_bytes);
   g.M = a.M; g.N = a.N; g.K = a.K;
   g.splits = a.splits; g.kt_per_split = a.kt_per_split;
-  g.ws = a.ws; g.cnt = a.cnt;
+  g.ws = a.ws;
   g.cfg = p.cfg;
   const int r = kind == Kind::Fwd ? gemm2_fwd(st, g) : kind == Kind::Dgrad ? gemm2_dgrad(st, g) : gemm2_wgrad(st, g);
   return r == 0 ? SL_OK : SL_EHIP;
@@ -520,10 +503,20 @@ int bind_workspace(Args& a, const Plan& p, int64_t M, int64_t N, void* ws, size_
   a.kt_per_split = p.kps;
   if (p.splits > 1) {
     if (!ws || ws_bytes < plan_ws_bytes(p, M, N) || !aligned16(ws)) return SL_EWORKSPACE;
-    a.cnt = static_cast<unsigned*>(ws);
-    a.ws = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+    a.ws = static_cast<float*>(ws);
   }
   return SL_OK;
+}
+
+// Second half of a split-K weight gradient: main_grad += the partial planes, in split order.
+int reduce_splits(hipStream_t st, const Args& a) {
+  if (a.splits <= 1) return SL_OK;
+  const int64_t n4 = int64_t(a.M) * (a.N / 4);
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(splitk_reduce, dim3(unsigned(blocks)), dim3(256), 0, st, static_cast<float*>(a.c), a.ldc,
+                     static_cast<const float*>(a.ws), a.M, a.N, a.splits);
+  return hipGetLastError() == hipSuccess ? SL_OK : SL_EHIP;
 }
 
 Args base_args(int64_t M, int64_t N, int64_t K, const Plan& p) {
@@ -608,8 +601,9 @@ extern "C" int sl_linear_wgrad_accum(void* stream, const void* X, const void* dY
   st = bind_workspace(a, p, out, in, workspace, workspace_bytes);
   if (st) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (p.v2) return run_v2(hs, Kind::Wgrad, a, p, T * out * 2, T * in * 2);
-  return run_v1<false, false, Elem::BF16, Elem::BF16, Epi::AccumF32>(hs, a, p);
+  st = p.v2 ? run_v2(hs, Kind::Wgrad, a, p, T * out * 2, T * in * 2)
+            : run_v1<false, false, Elem::BF16, Elem::BF16, Epi::AccumF32>(hs, a, p);
+  return st ? st : reduce_splits(hs, a);
 }
 
 extern "C" int sl_linear_fwd_mxfp8(void* stream, const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
@@ -663,5 +657,7 @@ extern "C" int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, con
   a.ldc = in;
   st = bind_workspace(a, p, out, in, workspace, workspace_bytes);
   if (st) return st;
-  return run_v1<false, false, Elem::BF16, Elem::MXFP8, Epi::AccumF32>(static_cast<hipStream_t>(stream), a, p);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  st = run_v1<false, false, Elem::BF16, Elem::MXFP8, Epi::AccumF32>(hs, a, p);
+  return st ? st : reduce_splits(hs, a);
 }

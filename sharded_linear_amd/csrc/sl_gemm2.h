@@ -13,12 +13,11 @@ struct Gemm2Args {
   int M, N, K;
   int tiles_m, tiles_n;
   int splits, kt_per_split;
-  float* ws;            // split-K partial tiles (accumulating kernel)
-  unsigned* cnt;        // split-K arrival counters
+  float* ws;            // split-K partial planes [splits][M][N] (accumulating kernel)
   int cfg;              // tile configuration, see gemm2_tile()
 };
 
-constexpr int kGemm2Configs = 7;
+constexpr int kGemm2Configs = 9;
 
 // A K-major (k contiguous) and B K-major: forward.
 int gemm2_fwd(hipStream_t st, Gemm2Args g);
@@ -26,5 +25,5 @@ int gemm2_fwd(hipStream_t st, Gemm2Args g);
 int gemm2_dgrad(hipStream_t st, Gemm2Args g);
 // A and B MN-major, fp32 accumulate into C: wgrad.
 int gemm2_wgrad(hipStream_t st, Gemm2Args g);
-// Macro-tile of configuration cfg.
-void gemm2_tile(int cfg, int* bm, int* bn);
+// Macro-tile (and k extent of one LDS stage) of configuration cfg.
+void gemm2_tile(int cfg, int* bm, int* bn, int* bk);

@@ -247,49 +247,12 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
         }
       }
   } else {
-    float* C = static_cast<float*>(g.c);
-    constexpr int NT = WAVES * 64;
-    if (g.splits > 1) {
-      __shared__ int last_flag;
-      constexpr int V = TM * TN * 4;
-      const int tile = tm * g.tiles_n + tn;
-      // Partials travel through device-coherent (agent-scope) relaxed atomic stores and loads,
-      // which bypass the per-XCD L2 state; each thread drains its stores (vmcnt 0) before the
-      // barrier that precedes the arrival count, so the last arriver sees every partial.  No
-      // cache-wide writeback or invalidate is needed, and co-resident blocks keep their L2.
-      float* mine = g.ws + (int64_t(tile) * g.splits + split) * V * 4 * NT;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            __hip_atomic_store(mine + ((i * TN + j) * 16 + r) * NT + tid, acc[i][j][r], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(g.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (prev == unsigned(g.splits - 1));
-      }
-      __syncthreads();
-      if (!last_flag) return;
-      const float* base = g.ws + int64_t(tile) * g.splits * V * 4 * NT;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float sum = 0.f;
-            for (int sp = 0; sp < g.splits; ++sp)
-              sum += sp == split ? acc[i][j][r]
-                                 : __hip_atomic_load(base + (int64_t(sp) * V * 4 + (i * TN + j) * 16 + r) * NT + tid,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            acc[i][j][r] = sum;
-          }
-      if (tid == 0) __hip_atomic_store(g.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // Unsplit: the single fp32 read-modify-write of main_grad.  Split-K: this split's partial
+    // goes to its own plane ws[split][M][N] with plain stores; the reduce kernel launched next
+    // on the stream adds the planes in split order into main_grad.
+    const bool direct = g.splits == 1;
+    float* C = direct ? static_cast<float*>(g.c) : g.ws + int64_t(split) * g.M * g.N;
+    const int64_t ldc = direct ? g.ldc : g.N;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -299,8 +262,8 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + rib + (r & 3);
           if (m < g.M && n < g.N) {
-            float* p = C + int64_t(m) * g.ldc + n;
-            *p = *p + acc[i][j][r];
+            float* p = C + int64_t(m) * ldc + n;
+            *p = direct ? *p + acc[i][j][r] : acc[i][j][r];
           }
         }
       }
@@ -336,6 +299,8 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
 //   4: 128x256, BK 64, 2 stages, 4 waves (64x128 wave tiles)      LDS  96 KiB
 //   5: 256x256, BK 64, 2 stages, 8 waves 2x4 (128x64 wave tiles)  LDS 128 KiB
 //   6: 256x256, BK 64, 2 stages, 8 waves 4x2 (64x128 wave tiles)  LDS 128 KiB
+//   7: 256x256, BK 32, 4 stages, 8 waves 2x4 (128x64 wave tiles)  LDS 128 KiB
+//   8: 256x256, BK 32, 3 stages, 8 waves 2x4 (128x64 wave tiles)  LDS  96 KiB
 #define SL2_DISPATCH(AK, BKM, ACC)                                                                 \
   switch (g.cfg) {                                                                                 \
     case 0: return sl2::launch_cfg<256, 256, 32, 4, 2, 2, AK, BKM, ACC>(st, g);                   \
@@ -345,6 +310,8 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
     case 4: return sl2::launch_cfg<128, 256, 64, 2, 2, 2, AK, BKM, ACC>(st, g);                   \
     case 5: return sl2::launch_cfg<256, 256, 64, 2, 2, 4, AK, BKM, ACC>(st, g);                   \
     case 6: return sl2::launch_cfg<256, 256, 64, 2, 4, 2, AK, BKM, ACC>(st, g);                   \
+    case 7: return sl2::launch_cfg<256, 256, 32, 4, 2, 4, AK, BKM, ACC>(st, g);                   \
+    case 8: return sl2::launch_cfg<256, 256, 32, 3, 2, 4, AK, BKM, ACC>(st, g);                   \
     default: return -1;                                                                            \
   }
 
@@ -352,8 +319,10 @@ int gemm2_fwd(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, true, false) }
 int gemm2_dgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, false, false) }
 int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) }
 
-void gemm2_tile(int cfg, int* bm, int* bn) {
-  static const int t[7][2] = {{256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256}, {256, 256}};
+void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
+  *bk = (cfg == 0 || cfg == 7 || cfg == 8) ? 32 : 64;
+  static const int t[9][2] = {{256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256},
+                              {256, 256}, {256, 256}, {256, 256}, {256, 256}};
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }

@@ -173,12 +173,13 @@ def test_neighbours_and_padding_untouched():
 
 
 def test_workspace_reused_across_shapes():
-    """One workspace serves split-K calls of different shapes in any order."""
+    """One workspace serves split-K calls of different shapes in any order; its initial contents
+    (here all-ones bytes, a NaN pattern for fp32) never reach the result."""
     say("case workspace reuse")
     cases = [(4104, 264, 520), (1000, 2056, 264), (4100, 288, 3336), (4104, 264, 520)]
     need = max(sl.sl_wgrad_workspace_bytes(*c) for c in cases)
     assert all(sl.sl_wgrad_workspace_bytes(*c) > 0 for c in cases)
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
     for T, n_in, n_out in cases:
         X, W, dY = rand_case(T, n_in, n_out, 77)
         G = torch.zeros((n_out, n_in), device="cuda")
@@ -187,7 +188,6 @@ def test_workspace_reused_across_shapes():
         e = ol.rel_err(host_f64(G), ol.linear_wgrad(X, dY))
         say(f"  T={T} in={n_in} out={n_out} rel err {e:.2e}")
         assert e <= TOL_F32
-    assert int(torch.count_nonzero(ws[:65536])) == 0        # counters left zero
 
 
 def test_wgrad_is_deterministic():
