@@ -44,6 +44,25 @@ def parse():
     return p.parse_args()
 
 
+def stored_traffic(workload_key: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter record of this
+    workload (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none or the kernel
+    sources have changed since the counters were taken."""
+    import glob
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_key}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "sharded_linear_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    if h.hexdigest() != rec.get("kernel_sources_sha256"):
+        return None
+    b = rec.get("per_launch_bytes", {}).get(kernel)
+    return None if b is None else int(b["fetch"] + b["write"])
+
+
 def copy_calibration(nbytes: int) -> None:
     """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE counter readings
     convert the counters of the GEMM kernels into HBM bytes."""
@@ -189,7 +208,8 @@ def main():
         d = gemm[dom]
         ach = d["flops"] / (d["ms"] * 1e-3) / 1e12
         roofline = {"kernel": f"linear_{dom}", "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                    "traffic": stored_traffic(w.key, f"linear_{dom}"),
                     "per_launch_flops": d["flops"] // d["launches"], "avg_launch_us": round(d["ms"] / d["launches"] * 1e3, 2)}
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload ----------------
