@@ -215,24 +215,36 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
     }
     const char* la = smem + (it % S) * kStage;
     const char* lb = la + OA::kBytes;
+    // fragments double-buffered in registers: the reads for k16 step ks+1 are in flight while
+    // the MFMAs of step ks issue
+    bf16x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(la, wm * WM + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(lb, wn * WN + j * 32, 0, lane);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 fa[TM], fb[TN];
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = OA::frag(la, wm * WM + i * 32, ks, lane);
+        for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = OA::frag(la, wm * WM + i * 32, ks + 1, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = OB::frag(lb, wn * WN + j * 32, ks, lane);
+        for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = OB::frag(lb, wn * WN + j * 32, ks + 1, lane);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
     }
   }
   wait_vmcnt<0>();
 
   // ---- epilogue ----------------------------------------------------------------------------
+  // Lane l holds column l%32 of each 32x32 block, rows 8*(r/4) + 4*(l/32) + r%4.  Tiles fully
+  // inside the matrix take a branch-free path (loads of a block batched before its adds).
   const int rib = 4 * (lane >> 5), cib = lane & 31;
+  const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
   if constexpr (!ACC) {
     __bf16* C = static_cast<__bf16*>(g.c);
 #pragma unroll
@@ -240,10 +252,17 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int n = n0 + wn * WN + j * 32 + cib;
+        const int mb = m0 + wm * WM + i * 32 + rib;
+        if (interior) {
+          __bf16* p = C + int64_t(mb) * g.ldc + n;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + rib + (r & 3);
-          if (m < g.M && n < g.N) C[int64_t(m) * g.ldc + n] = static_cast<__bf16>(acc[i][j][r]);
+          for (int r = 0; r < 16; ++r) p[int64_t(8 * (r >> 2) + (r & 3)) * g.ldc] = static_cast<__bf16>(acc[i][j][r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = mb + 8 * (r >> 2) + (r & 3);
+            if (m < g.M && n < g.N) C[int64_t(m) * g.ldc + n] = static_cast<__bf16>(acc[i][j][r]);
+          }
         }
       }
   } else {
@@ -258,12 +277,27 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int n = n0 + wn * WN + j * 32 + cib;
+        const int mb = m0 + wm * WM + i * 32 + rib;
+        if (interior) {
+          float* p = C + int64_t(mb) * ldc + n;
+          if (direct) {
+            float old[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + rib + (r & 3);
-          if (m < g.M && n < g.N) {
-            float* p = C + int64_t(m) * ldc + n;
-            *p = direct ? *p + acc[i][j][r] : acc[i][j][r];
+            for (int r = 0; r < 16; ++r) old[r] = p[int64_t(8 * (r >> 2) + (r & 3)) * ldc];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[int64_t(8 * (r >> 2) + (r & 3)) * ldc] = old[r] + acc[i][j][r];
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[int64_t(8 * (r >> 2) + (r & 3)) * ldc] = acc[i][j][r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = mb + 8 * (r >> 2) + (r & 3);
+            if (m < g.M && n < g.N) {
+              float* p = C + int64_t(m) * ldc + n;
+              *p = direct ? *p + acc[i][j][r] : acc[i][j][r];
+            }
           }
         }
       }
