@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "sl_gemm2.h"
 
@@ -87,11 +88,11 @@ struct KMaj {
   }
 
   // Wave `w` issues loads wl = w, w + waves, ...; lane i fills LDS bytes [1024 wl + 16 i, +16).
-  template <int WAVES>
+  template <int WAVES, int LO = 0, int HI = kLoads / WAVES>
   __device__ static __forceinline__ void load(i32x4 rs, char* lds, int lane, int wave,
                                               int row0, int rows, int k0, int K, int64_t ld) {
 #pragma unroll
-    for (int it = 0; it < kLoads / WAVES; ++it) {
+    for (int it = LO; it < HI; ++it) {
       const int wl = it * WAVES + wave;
       const int p = wl * 64 + lane;                      // 16-byte slot
       const int r = p / kCPR, c = (p % kCPR) ^ swz(p / kCPR);
@@ -122,11 +123,11 @@ struct MNMaj {
   // pairs are pair ^ {0, 5, 2, 7}, distinct within 128- and 256-byte bank windows.
   __device__ static __forceinline__ int swz(int k) { return ((k & 3) ^ ((k & 1) << 2)) << 1; }
 
-  template <int WAVES>
+  template <int WAVES, int LO = 0, int HI = kLoads / WAVES>
   __device__ static __forceinline__ void load(i32x4 rs, char* lds, int lane, int wave,
                                               int col0, int cols, int k0, int K, int64_t ld) {
 #pragma unroll
-    for (int it = 0; it < kLoads / WAVES; ++it) {
+    for (int it = LO; it < HI; ++it) {
       const int wl = it * WAVES + wave;
       const int p = wl * 64 + lane;
       const int k = p / kCPR, c = (p % kCPR) ^ swz(p / kCPR);
@@ -150,12 +151,26 @@ struct MNMaj {
   }
 };
 
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// Calls f(ic<0>), ..., f(ic<N-1>): a compile-time loop.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(ic<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 template <bool KM, int R, int BK>
 struct OpSel { using T = KMaj<R, BK>; };
 template <int R, int BK>
 struct OpSel<false, R, BK> { using T = MNMaj<R, BK>; };
 
-template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC>
+// SCHED 0 leaves instruction order to the compiler; SCHED 1 asks it (sched_group_barrier) to
+// alternate MFMAs with the LDS fragment reads of the next k16 step.
+template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED>
 __global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
   constexpr int WAVES = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
@@ -193,6 +208,22 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
     OA::template load<WAVES>(ra, base, lane, wave, m0, g.M, k0, g.K, g.lda);
     OB::template load<WAVES>(rb, base + OA::kBytes, lane, wave, n0, g.N, k0, g.K, g.ldb);
   };
+  // The loads of one stage, split into BK/16 parts issued one per k16 step of the loop.
+  constexpr int NP = BK / 16;
+  constexpr int LA = OA::kLoads / WAVES, LB = OB::kLoads / WAVES;
+  constexpr bool kSpread = LA % NP == 0 && LB % NP == 0;
+  auto issue_part = [&](int kt, int slot, auto part) {
+    constexpr int P = decltype(part)::value;
+    char* base = smem + slot * kStage;
+    const int k0 = kt * BK;
+    if constexpr (kSpread) {
+      OA::template load<WAVES, P * LA / NP, (P + 1) * LA / NP>(ra, base, lane, wave, m0, g.M, k0, g.K, g.lda);
+      OB::template load<WAVES, P * LB / NP, (P + 1) * LB / NP>(rb, base + OA::kBytes, lane, wave, n0, g.N, k0, g.K, g.ldb);
+    } else if constexpr (P == 0) {
+      OA::template load<WAVES>(ra, base, lane, wave, m0, g.M, k0, g.K, g.lda);
+      OB::template load<WAVES>(rb, base + OA::kBytes, lane, wave, n0, g.N, k0, g.K, g.ldb);
+    }
+  };
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -209,23 +240,22 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
   for (int it = 0; it < nk; ++it) {
     wait_vmcnt<(S - 2) * kLoadsPerThread>();
     __syncthreads();
-    {
-      const int nxt = it + S - 1;
-      issue(kt0 + (nxt < nk ? nxt : nk), nxt % S);
-    }
+    const int nxt = it + S - 1;
+    const int kt_next = kt0 + (nxt < nk ? nxt : nk), slot_next = nxt % S;
     const char* la = smem + (it % S) * kStage;
     const char* lb = la + OA::kBytes;
     // fragments double-buffered in registers: the reads for k16 step ks+1 are in flight while
-    // the MFMAs of step ks issue
+    // the MFMAs of step ks issue; the next stage's HBM->LDS loads are spread over the steps
     bf16x8 fa[2][TM], fb[2][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(la, wm * WM + i * 32, 0, lane);
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(lb, wn * WN + j * 32, 0, lane);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < BK / 16) {
+    static_for<NP>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
+      constexpr int cur = ks & 1;
+      issue_part(kt_next, slot_next, ksc);
+      if constexpr (ks + 1 < NP) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = OA::frag(la, wm * WM + i * 32, ks + 1, lane);
 #pragma unroll
@@ -236,7 +266,16 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
-    }
+      if constexpr (SCHED == 1 && ks + 1 < NP) {
+        constexpr int kDs = TM * (A_KM ? 1 : 2) + TN * (B_KM ? 1 : 2);
+#pragma unroll
+        for (int q = 0; q < TM * TN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (q < kDs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (kDs > TM * TN) __builtin_amdgcn_sched_group_barrier(0x100, kDs - TM * TN, 0);
+      }
+    });
   }
   wait_vmcnt<0>();
 
@@ -304,12 +343,12 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
   }
 }
 
-template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC>
+template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED = 0>
 int launch_cfg(hipStream_t st, Gemm2Args g) {
   using OA = typename OpSel<A_KM, BM, BK>::T;
   using OB = typename OpSel<B_KM, BN, BK>::T;
   constexpr int lds = S * (OA::kBytes + OB::kBytes);
-  auto kfn = gemm2<BM, BN, BK, S, WGM, WGN, A_KM, B_KM, ACC>;
+  auto kfn = gemm2<BM, BN, BK, S, WGM, WGN, A_KM, B_KM, ACC, SCHED>;
   static bool attr = false;
   if (!attr) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
@@ -335,6 +374,9 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
 //   6: 256x256, BK 64, 2 stages, 8 waves 4x2 (64x128 wave tiles)  LDS 128 KiB
 //   7: 256x256, BK 32, 4 stages, 8 waves 2x4 (128x64 wave tiles)  LDS 128 KiB
 //   8: 256x256, BK 32, 3 stages, 8 waves 2x4 (128x64 wave tiles)  LDS  96 KiB
+//   9: as 1 (4 waves, 128x128 wave tiles) with MFMA / LDS-read interleaving
+//  10: as 5 with MFMA / LDS-read interleaving
+//  11: as 6 with MFMA / LDS-read interleaving
 #define SL2_DISPATCH(AK, BKM, ACC)                                                                 \
   switch (g.cfg) {                                                                                 \
     case 0: return sl2::launch_cfg<256, 256, 32, 4, 2, 2, AK, BKM, ACC>(st, g);                   \
@@ -346,6 +388,9 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
     case 6: return sl2::launch_cfg<256, 256, 64, 2, 4, 2, AK, BKM, ACC>(st, g);                   \
     case 7: return sl2::launch_cfg<256, 256, 32, 4, 2, 4, AK, BKM, ACC>(st, g);                   \
     case 8: return sl2::launch_cfg<256, 256, 32, 3, 2, 4, AK, BKM, ACC>(st, g);                   \
+    case 9: return sl2::launch_cfg<256, 256, 64, 2, 2, 2, AK, BKM, ACC, 1>(st, g);                \
+    case 10: return sl2::launch_cfg<256, 256, 64, 2, 2, 4, AK, BKM, ACC, 1>(st, g);               \
+    case 11: return sl2::launch_cfg<256, 256, 64, 2, 4, 2, AK, BKM, ACC, 1>(st, g);               \
     default: return -1;                                                                            \
   }
 
@@ -355,8 +400,8 @@ int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) 
 
 void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
   *bk = (cfg == 0 || cfg == 7 || cfg == 8) ? 32 : 64;
-  static const int t[9][2] = {{256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256},
-                              {256, 256}, {256, 256}, {256, 256}, {256, 256}};
+  static const int t[12][2] = {{256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256},
+                               {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}};
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }
