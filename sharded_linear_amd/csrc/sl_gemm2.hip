@@ -170,8 +170,8 @@ struct OpSel<false, R, BK> { using T = MNMaj<R, BK>; };
 
 // SCHED 0 leaves instruction order to the compiler; SCHED 1 asks it (sched_group_barrier) to
 // alternate MFMAs with the LDS fragment reads of the next k16 step.
-template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED>
-__global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
+template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED, int OCC>
+__global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
   constexpr int WAVES = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
   using OA = typename OpSel<A_KM, BM, BK>::T;
@@ -343,12 +343,12 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm2(Gemm2Args g) {
   }
 }
 
-template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED = 0>
+template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED = 0, int OCC = 1>
 int launch_cfg(hipStream_t st, Gemm2Args g) {
   using OA = typename OpSel<A_KM, BM, BK>::T;
   using OB = typename OpSel<B_KM, BN, BK>::T;
   constexpr int lds = S * (OA::kBytes + OB::kBytes);
-  auto kfn = gemm2<BM, BN, BK, S, WGM, WGN, A_KM, B_KM, ACC, SCHED>;
+  auto kfn = gemm2<BM, BN, BK, S, WGM, WGN, A_KM, B_KM, ACC, SCHED, OCC>;
   static bool attr = false;
   if (!attr) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
@@ -377,6 +377,9 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
 //   9: as 1 (4 waves, 128x128 wave tiles) with MFMA / LDS-read interleaving
 //  10: as 5 with MFMA / LDS-read interleaving
 //  11: as 6 with MFMA / LDS-read interleaving
+//  12: 256x128, BK 32, 2 stages, 4 waves (128x64 wave tiles), 2 workgroups per CU   LDS 48 KiB
+//  13: 128x256, BK 32, 2 stages, 4 waves (64x128 wave tiles), 2 workgroups per CU   LDS 48 KiB
+//  14: 256x128, BK 32, 3 stages, 4 waves (128x64 wave tiles), 2 workgroups per CU   LDS 72 KiB
 #define SL2_DISPATCH(AK, BKM, ACC)                                                                 \
   switch (g.cfg) {                                                                                 \
     case 0: return sl2::launch_cfg<256, 256, 32, 4, 2, 2, AK, BKM, ACC>(st, g);                   \
@@ -391,6 +394,9 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
     case 9: return sl2::launch_cfg<256, 256, 64, 2, 2, 2, AK, BKM, ACC, 1>(st, g);                \
     case 10: return sl2::launch_cfg<256, 256, 64, 2, 2, 4, AK, BKM, ACC, 1>(st, g);               \
     case 11: return sl2::launch_cfg<256, 256, 64, 2, 4, 2, AK, BKM, ACC, 1>(st, g);               \
+    case 12: return sl2::launch_cfg<256, 128, 32, 2, 2, 2, AK, BKM, ACC, 0, 2>(st, g);            \
+    case 13: return sl2::launch_cfg<128, 256, 32, 2, 2, 2, AK, BKM, ACC, 0, 2>(st, g);            \
+    case 14: return sl2::launch_cfg<256, 128, 32, 3, 2, 2, AK, BKM, ACC, 0, 2>(st, g);            \
     default: return -1;                                                                            \
   }
 
@@ -399,9 +405,10 @@ int gemm2_dgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, false, false) 
 int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) }
 
 void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
-  *bk = (cfg == 0 || cfg == 7 || cfg == 8) ? 32 : 64;
-  static const int t[12][2] = {{256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256},
-                               {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}};
+  *bk = (cfg == 0 || cfg == 7 || cfg == 8 || cfg >= 12) ? 32 : 64;
+  static const int t[15][2] = {{256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256},
+                               {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256},
+                               {256, 128}, {128, 256}, {256, 128}};
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }
