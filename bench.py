@@ -129,7 +129,7 @@ def main():
     wss = {}
     for n in names:
         o, i = w.params[n]
-        nb = sl.sl_wgrad_workspace_bytes(T, i, o)
+        nb = sl.sl_mxfp8_workspace_bytes(T, i, o) if w.mxfp8 else sl.sl_wgrad_workspace_bytes(T, i, o)
         wss[n] = torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev) if nb else None
     torch.cuda.synchronize()
     log(f"set-up {time.time() - t0:.1f}s: {w.title}; grad_data {buf.numel} elements")
@@ -163,7 +163,7 @@ def main():
                 o, i = w.params[n]
                 f = 2 * T * i * o
                 if w.mxfp8:
-                    launch("dgrad", f, sl.sl_linear_dgrad_mxfp8w, dys[k][n], *wq[n], dxs[n], timed=timed)
+                    launch("dgrad", f, sl.sl_linear_dgrad_mxfp8w, dys[k][n], *wq[n], dxs[n], wss[n], timed=timed)
                     launch("wgrad", f, sl.sl_linear_wgrad_accum_mxfp8x, *xs[k][n], dys[k][n],
                            buf.main_grad(n), wss[n], timed=timed)
                 else:
@@ -184,8 +184,10 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     flops = w.flops_per_step()
     tflops = flops / (ms * 1e-3) / 1e12
-    dtype = "bf16"        # the MXFP8 operands are dequantised exactly to bf16 and run bf16 MFMA
-    peak = PEAK_TFLOPS[dtype]
+    # MXFP8 workload: fwd runs block-scaled fp8 MFMA, dgrad/wgrad bf16 MFMA on the exactly
+    # dequantised operand; the bf16 peak is the conservative denominator for the whole step.
+    dtype = "mxfp8-e4m3 fwd / bf16 bwd" if w.mxfp8 else "bf16"
+    peak = PEAK_TFLOPS["bf16"]
 
     # ---- per-kernel figures from the events -----------------------------------------------
     kinds = {}
@@ -207,8 +209,9 @@ def main():
         dom = max(gemm, key=lambda k: gemm[k]["ms"])
         d = gemm[dom]
         ach = d["flops"] / (d["ms"] * 1e-3) / 1e12
-        roofline = {"kernel": f"linear_{dom}", "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+        kpeak = PEAK_TFLOPS["fp8"] if (w.mxfp8 and dom == "fwd") else peak
+        roofline = {"kernel": f"linear_{dom}", "bound": "mfma", "achieved": round(ach, 1), "peak": kpeak,
+                    "unit": "TFLOP/s", "frac": round(ach / kpeak, 4),
                     "traffic": stored_traffic(w.key, f"linear_{dom}"),
                     "per_launch_flops": d["flops"] // d["launches"], "avg_launch_us": round(d["ms"] / d["launches"] * 1e3, 2)}
 

@@ -117,17 +117,25 @@ int sl_linear_wgrad_accum(void* stream, const void* X, const void* dY, float* ma
  * section 1.3: E4M3 elements with one E8M0 scale per 32 elements).  A quantised matrix M[r, c]
  * is passed as codes Mq[r, c] (uint8, E4M3FN) and scales Ms[r, c/32] (uint8, E8M0), and stands
  * for deq(q, s) = E4M3(q) * 2^(s - 127).  Blocks run along `in` for both X and W.
- *   fwd:   Y  = deq(Xq).deq(Wq)^T           (bf16 out)
+ *   fwd:   Y  = deq(Xq).deq(Wq)^T           (bf16 out; block-scaled fp8 MFMA when 128 | in and
+ *                                            the scale pointers are 4-byte aligned)
  *   dgrad: dX = dY.deq(Wq)                  (dY, dX bf16)
  *   wgrad: main_grad += dY^T.deq(Xq)        (dY bf16, main_grad fp32)
  * Every dequantised element must be representable in bf16 (an E4M3 value times a power of two
  * whose result is a normal bf16); it then enters the GEMMs exactly.  in must be a multiple of
- * 32.  The wgrad workspace contract is the one of sl_linear_wgrad_accum.
+ * 32.  Code pointers must be 16-byte aligned; scale pointers have no alignment requirement.
+ *
+ * dgrad and wgrad take a device workspace of at least sl_mxfp8_workspace_bytes(T, in, out)
+ * bytes: the MXFP8 operand is dequantised into its front (bf16), the rest serves the bf16
+ * weight-gradient split-K planes.  Its initial contents do not matter; calls that may run
+ * concurrently must use distinct workspaces.
  * ------------------------------------------------------------------------------------------- */
+size_t sl_mxfp8_workspace_bytes(int64_t T, int64_t in, int64_t out);
 int sl_linear_fwd_mxfp8(void* stream, const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
                         const uint8_t* Ws, void* Y, int64_t T, int64_t in, int64_t out);
 int sl_linear_dgrad_mxfp8w(void* stream, const void* dY, const uint8_t* Wq, const uint8_t* Ws,
-                           void* dX, int64_t T, int64_t in, int64_t out);
+                           void* dX, int64_t T, int64_t in, int64_t out,
+                           void* workspace, size_t workspace_bytes);
 int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, const uint8_t* Xs,
                                  const void* dY, float* main_grad, int64_t T, int64_t in,
                                  int64_t out, void* workspace, size_t workspace_bytes);

@@ -32,7 +32,9 @@
 #include <cstring>
 
 #include "sharded_linear.h"
+#include "sl_device.h"
 #include "sl_gemm2.h"
+#include "sl_gemm_f8.h"
 
 namespace {
 
@@ -65,29 +67,6 @@ struct Args {
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// E4M3FN code times 2^(s - 127) as bf16 bits.  Value = sig * 2^(max(e,1) - 10) with
-// sig = 8 + m for normals (e > 0) and sig = m for subnormals; exact whenever the result is a
-// normal bf16 (the caller's contract); NaN codes or the NaN scale give a quiet NaN.
-__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t code, uint32_t s) {
-  const uint32_t sign = (code & 0x80u) << 8;
-  const uint32_t e = (code >> 3) & 0xFu, m = code & 0x7u;
-  if ((code & 0x7Fu) == 0x7Fu || s == 0xFFu) return sign | 0x7FC0u;
-  if ((code & 0x7Fu) == 0) return sign;
-  int exp;
-  uint32_t mant;
-  if (e) {
-    exp = int(e) + int(s) - 7;
-    mant = m << 4;
-  } else {
-    const int p = 31 - __builtin_clz(m);            // leading bit of the subnormal field
-    exp = p + int(s) - 9;
-    mant = ((m << (3 - p)) & 0x7u) << 4;
-  }
-  if (exp <= 0) return sign;                        // outside the contract: flush
-  if (exp >= 255) return sign | 0x7F80u;
-  return sign | (uint32_t(exp) << 7) | mant;
-}
-
 // Eight E4M3 codes (one 8-byte chunk) with their block scale -> eight bf16 in a 16-byte chunk.
 __device__ __forceinline__ uint4 dequant8(uint2 q, uint32_t s) {
   uint32_t w[4];
@@ -95,7 +74,7 @@ __device__ __forceinline__ uint4 dequant8(uint2 q, uint32_t s) {
   for (int i = 0; i < 4; ++i) {
     const uint32_t src = i < 2 ? q.x : q.y;
     const int sh = (i & 1) * 16;
-    w[i] = e4m3_to_bf16((src >> sh) & 0xFFu, s) | (e4m3_to_bf16((src >> (sh + 8)) & 0xFFu, s) << 16);
+    w[i] = sl2::e4m3_to_bf16((src >> sh) & 0xFFu, s) | (sl2::e4m3_to_bf16((src >> (sh + 8)) & 0xFFu, s) << 16);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
@@ -466,10 +445,7 @@ size_t plan_ws_bytes(const Plan& p, int64_t M, int64_t N) {
 // weight-gradient GEMM: M = out, N = in, K = T; A = dY [T, out], B = X [T, in] (bf16 or MXFP8)
 size_t wgrad_ws_bytes(int64_t T, int64_t in, int64_t out) {
   if (T <= 0 || in <= 0 || out <= 0) return 0;
-  const Plan pb = make_plan(Kind::Wgrad, false, out, in, T, T * out * 2, T * in * 2);
-  const Plan pq = make_plan(Kind::Wgrad, true, out, in, T, T * out * 2, T * in);
-  const size_t a = plan_ws_bytes(pb, out, in), b = plan_ws_bytes(pq, out, in);
-  return a > b ? a : b;
+  return plan_ws_bytes(make_plan(Kind::Wgrad, false, out, in, T, T * out * 2, T * in * 2), out, in);
 }
 
 template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, Elem EA, Elem EB, Epi EPI>
@@ -608,6 +584,45 @@ extern "C" int sl_linear_wgrad_accum(void* stream, const void* X, const void* dY
   return st ? st : reduce_splits(hs, a);
 }
 
+// ---- MXFP8 operand entry points -----------------------------------------------------------
+// The native paths need 128 | in (whole 4-block scale dwords per stage) and dword-aligned scale
+// rows; other shapes take the register-staged kernels, which dequantise in registers.
+
+namespace {
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool f8_native(int64_t T, int64_t in, int64_t out, const void* Xs, const void* Ws) {
+  return in % 128 == 0 && aligned4(Xs) && aligned4(Ws) && T * in <= kMaxDmaBytes && out * in <= kMaxDmaBytes;
+}
+
+// Dequantised operand (bf16) at the front of an MXFP8 workspace, then the bf16 split-K planes.
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+
+bool mx_bf16_path(int64_t rows, int64_t in, int64_t other_bytes) {
+  return in % 32 == 0 && rows * in * 2 <= kMaxDmaBytes && other_bytes <= kMaxDmaBytes;
+}
+
+}  // namespace
+
+extern "C" size_t sl_mxfp8_workspace_bytes(int64_t T, int64_t in, int64_t out) {
+  if (T <= 0 || in <= 0 || out <= 0 || in % 32) return 0;
+  size_t need = 0;
+  // dgrad: W [out, in] dequantised
+  if (mx_bf16_path(out, in, T * out * 2)) need = size_t(round256(out * in * 2));
+  // wgrad: X [T, in] dequantised, plus the bf16 plan's split planes
+  if (mx_bf16_path(T, in, T * out * 2)) {
+    const Plan p = make_plan(Kind::Wgrad, false, out, in, T, T * out * 2, T * in * 2);
+    const size_t w = size_t(round256(T * in * 2)) + plan_ws_bytes(p, out, in);
+    if (w > need) need = w;
+  } else {
+    const Plan p = make_plan(Kind::Wgrad, true, out, in, T, T * out * 2, T * in);
+    const size_t w = plan_ws_bytes(p, out, in);
+    if (w > need) need = w;
+  }
+  return need;
+}
+
 extern "C" int sl_linear_fwd_mxfp8(void* stream, const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
                                    const uint8_t* Ws, void* Y, int64_t T, int64_t in, int64_t out) {
   int st = check_dims(T, in, out, 8);
@@ -616,30 +631,48 @@ extern "C" int sl_linear_fwd_mxfp8(void* stream, const uint8_t* Xq, const uint8_
   if (T == 0 || out == 0) return SL_OK;
   if (!Y || (in > 0 && (!Xq || !Xs || !Wq || !Ws))) return SL_EINVAL;
   if (!aligned16(Xq) || !aligned16(Wq) || !aligned16(Y)) return SL_EALIGN;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (in > 0 && f8_native(T, in, out, Xs, Ws)) {
+    F8Args g{};
+    g.a = Xq; g.b = Wq; g.sa = Xs; g.sb = Ws; g.c = Y;
+    g.lda = in; g.ldb = in; g.ldc = out;
+    g.a_bytes = uint32_t(T * in); g.b_bytes = uint32_t(out * in);
+    g.sa_bytes = uint32_t(T * (in / 32)); g.sb_bytes = uint32_t(out * (in / 32));
+    g.M = int(T); g.N = int(out); g.K = int(in);
+    g.cfg = ntiles(T, out, 256, 256) >= 200 ? 0 : 1;
+    return f8_fwd(hs, g) == 0 ? SL_OK : SL_EHIP;
+  }
   const Plan p = make_plan(Kind::Fwd, true, T, out, in, T * in, out * in);
   Args a = base_args(T, out, in, p);
   a.a = {Xq, Xs, in, int(T)};
   a.b = {Wq, Ws, in, int(out)};
   a.c = Y;
   a.ldc = out;
-  return run_v1<true, true, Elem::MXFP8, Elem::MXFP8, Epi::StoreBF16>(static_cast<hipStream_t>(stream), a, p);
+  return run_v1<true, true, Elem::MXFP8, Elem::MXFP8, Epi::StoreBF16>(hs, a, p);
 }
 
 extern "C" int sl_linear_dgrad_mxfp8w(void* stream, const void* dY, const uint8_t* Wq, const uint8_t* Ws,
-                                      void* dX, int64_t T, int64_t in, int64_t out) {
+                                      void* dX, int64_t T, int64_t in, int64_t out, void* workspace,
+                                      size_t workspace_bytes) {
   int st = check_dims(T, in, out, 8);
   if (st) return st;
   if (in % 32) return SL_ESHAPE;
   if (T == 0 || in == 0) return SL_OK;
   if (!dX || (out > 0 && (!dY || !Wq || !Ws))) return SL_EINVAL;
   if (!aligned16(dY) || !aligned16(Wq) || !aligned16(dX)) return SL_EALIGN;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (out > 0 && mx_bf16_path(out, in, T * out * 2)) {
+    if (!workspace || !aligned16(workspace) || workspace_bytes < size_t(round256(out * in * 2))) return SL_EWORKSPACE;
+    if (mx_dequant(hs, Wq, Ws, workspace, out, in)) return SL_EHIP;
+    return sl_linear_dgrad(stream, dY, workspace, dX, T, in, out);
+  }
   const Plan p = make_plan(Kind::Dgrad, true, T, in, out, T * out * 2, out * in);
   Args a = base_args(T, in, out, p);
   a.a = {dY, nullptr, out, int(T)};
   a.b = {Wq, Ws, in, int(in)};
   a.c = dX;
   a.ldc = in;
-  return run_v1<true, false, Elem::BF16, Elem::MXFP8, Epi::StoreBF16>(static_cast<hipStream_t>(stream), a, p);
+  return run_v1<true, false, Elem::BF16, Elem::MXFP8, Epi::StoreBF16>(hs, a, p);
 }
 
 extern "C" int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, const uint8_t* Xs, const void* dY,
@@ -651,6 +684,14 @@ extern "C" int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, con
   if (T == 0 || in == 0 || out == 0) return SL_OK;
   if (!Xq || !Xs || !dY || !main_grad) return SL_EINVAL;
   if (!aligned16(Xq) || !aligned16(dY) || !aligned16(main_grad)) return SL_EALIGN;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (mx_bf16_path(T, in, T * out * 2)) {
+    const int64_t xb = round256(T * in * 2);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < size_t(xb)) return SL_EWORKSPACE;
+    if (mx_dequant(hs, Xq, Xs, workspace, T, in)) return SL_EHIP;
+    return sl_linear_wgrad_accum(stream, workspace, dY, main_grad, T, in, out, static_cast<char*>(workspace) + xb,
+                                 workspace_bytes - size_t(xb));
+  }
   const Plan p = make_plan(Kind::Wgrad, true, out, in, T, T * out * 2, T * in);
   Args a = base_args(out, in, T, p);
   a.a = {dY, nullptr, out, int(out)};
@@ -659,7 +700,6 @@ extern "C" int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, con
   a.ldc = in;
   st = bind_workspace(a, p, out, in, workspace, workspace_bytes);
   if (st) return st;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
   st = run_v1<false, false, Elem::BF16, Elem::MXFP8, Epi::AccumF32>(hs, a, p);
   return st ? st : reduce_splits(hs, a);
 }

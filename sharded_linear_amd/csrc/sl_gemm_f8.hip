@@ -1,0 +1,254 @@
+// MXFP8 operand kernels of the linear step (gfx950).
+//
+// NVIDIA Megatron-Core guide "Generalized Tensor Parallelism", section 1.3: weights (and here
+// activations) travel as E4M3 elements with one E8M0 scale per 32 elements along `in`.
+//
+//  * fwd Y = deq(Xq) . deq(Wq)^T: both operands are blocked along the contraction axis, so the
+//    block-scaled fp8 MFMA v_mfma_scale_f32_32x32x64_f8f6f4 consumes the codes and scales
+//    directly.  Its operand layout (checked on the hardware): for a 64-wide k step, lane l of a
+//    32-row fragment holds row l%32; lane group g = l/32 carries elements [16g, 16g+16) in
+//    bytes 0..15 and [32+16g, 32+16g+16) in bytes 16..31, and the scale supplied by the lane of
+//    row m in group g multiplies the 32-element block g of that row.  So each lane loads the two
+//    16-byte chunks 16g and 32+16g of the k step and the scale of block (k0/32 + g).
+//    Codes travel HBM->LDS directly (buffer_load ... lds, rows of 128 bytes, swizzled like the
+//    bf16 tiles); each stage also carries one dword of 4 block scales per row.
+//  * dgrad / wgrad see the MXFP8 operand blocked along their N, not K; it is dequantised
+//    exactly into a bf16 workspace by mx_dequant_bf16 (an E4M3 value times a power of two has
+//    at most 4 significant bits) and the bf16 GEMM kernels run on it.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sl_device.h"
+#include "sl_gemm_f8.h"
+
+namespace sl2 {
+
+constexpr int kF8RowBytes = 128;      // fp8 k elements per LDS row per stage
+constexpr int kF8CPR = kF8RowBytes / 16;
+
+__device__ __forceinline__ int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int R>
+struct F8Tile {
+  static constexpr int kBytes = R * kF8RowBytes;
+  static constexpr int kLoads = kBytes / 1024;
+  static constexpr int kScaleBytes = R * 4;
+  static constexpr int kScaleLoads = (kScaleBytes + 255) / 256;
+
+  template <int WAVES>
+  static constexpr int kScaleLoadsPerWave = (kScaleLoads + WAVES - 1) / WAVES;
+
+  // Every wave issues kLoads/WAVES code loads and kScaleLoadsPerWave scale loads, so per-wave
+  // vmcnt arithmetic is uniform; surplus scale loads read out of range into `pad` (zeros).
+  template <int WAVES>
+  __device__ static __forceinline__ void load(i32x4 rs, i32x4 rss, char* lds, char* lds_s, char* pad, int lane,
+                                              int wave, int row0, int rows, int k0, int K, int64_t ld) {
+#pragma unroll
+    for (int it = 0; it < kLoads / WAVES; ++it) {
+      const int wl = it * WAVES + wave;
+      const int p = wl * 64 + lane;
+      const int r = p / kF8CPR, c = (p % kF8CPR) ^ swz128(p / kF8CPR);
+      const int gr = row0 + r, k = k0 + c * 16;
+      const uint32_t off = (gr < rows && k < K) ? uint32_t(int64_t(gr) * ld + k) : kOOB;
+      lds_dma16(rs, lds_addr(lds + wl * 1024), off);
+    }
+    // scale dwords: row r holds the E8M0 scales of blocks k0/32 .. k0/32+3
+    const int nb = K / 32;
+#pragma unroll
+    for (int it = 0; it < kScaleLoadsPerWave<WAVES>; ++it) {
+      const int wl = it * WAVES + wave;
+      if (wl < kScaleLoads) {
+        const int r = wl * 64 + lane;
+        const int gr = row0 + r, b = k0 / 32;
+        const uint32_t off = (r < R && gr < rows && b < nb) ? uint32_t(int64_t(gr) * nb + b) : kOOB;
+        lds_dma4(rss, lds_addr(lds_s + wl * 256), off);
+      } else {
+        lds_dma4(rss, lds_addr(pad), kOOB);
+      }
+    }
+  }
+  // 32 bytes of fragment row r0 + l%32 for k64 step ks: chunks 4ks+g and 4ks+2+g
+  __device__ static __forceinline__ i32x8 frag(const char* lds, int r0, int ks, int lane) {
+    const int r = r0 + (lane & 31), g = lane >> 5;
+    const char* row = lds + r * kF8RowBytes;
+    const uint4 lo = *reinterpret_cast<const uint4*>(row + (((4 * ks + g) ^ swz128(r)) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(row + (((4 * ks + 2 + g) ^ swz128(r)) << 4));
+    i32x8 v;
+    v[0] = int(lo.x); v[1] = int(lo.y); v[2] = int(lo.z); v[3] = int(lo.w);
+    v[4] = int(hi.x); v[5] = int(hi.y); v[6] = int(hi.z); v[7] = int(hi.w);
+    return v;
+  }
+  __device__ static __forceinline__ uint32_t scales(const char* lds_s, int r0, int lane) {
+    return *reinterpret_cast<const uint32_t*>(lds_s + (r0 + (lane & 31)) * 4);
+  }
+};
+
+template <int BM, int BN, int S, int WGM, int WGN>
+__global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
+  constexpr int WAVES = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
+  using TA = F8Tile<BM>;
+  using TB = F8Tile<BN>;
+  // stage layout: A codes | B codes | A scale dwords | B scale dwords | 256-byte pad
+  constexpr int kScaleOff = TA::kBytes + TB::kBytes;
+  constexpr int kPadOff = kScaleOff + ((TA::kScaleBytes + TB::kScaleBytes + 255) / 256) * 256;
+  constexpr int kStage = kPadOff + 256;
+  static_assert(TA::kLoads % WAVES == 0 && TB::kLoads % WAVES == 0, "loads per wave");
+  constexpr int kLoadsPerWave = (TA::kLoads + TB::kLoads) / WAVES + TA::template kScaleLoadsPerWave<WAVES> +
+                                TB::template kScaleLoadsPerWave<WAVES>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int t = xcd_remap(blockIdx.x, ntiles);
+  const int group = t / (8 * g.tiles_n);
+  const int first_m = group * 8;
+  const int gsz = min(g.tiles_m - first_m, 8);
+  const int tm = first_m + (t % (8 * g.tiles_n)) % gsz;
+  const int tn = (t % (8 * g.tiles_n)) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nk = (g.K + kF8RowBytes - 1) / kF8RowBytes;
+
+  const i32x4 ra = rsrc(g.a, g.a_bytes), rb = rsrc(g.b, g.b_bytes);
+  const i32x4 rsa = rsrc(g.sa, g.sa_bytes), rsb = rsrc(g.sb, g.sb_bytes);
+
+  auto issue = [&](int kt, int slot) {
+    char* base = smem + slot * kStage;
+    char* sbase = base + kScaleOff;
+    const int k0 = kt * kF8RowBytes;
+    TA::template load<WAVES>(ra, rsa, base, sbase, base + kPadOff, lane, wave, m0, g.M, k0, g.K, g.lda);
+    TB::template load<WAVES>(rb, rsb, base + TA::kBytes, sbase + TA::kScaleBytes, base + kPadOff, lane, wave, n0, g.N,
+                             k0, g.K, g.ldb);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s < nk ? s : nk, s);
+
+  for (int it = 0; it < nk; ++it) {
+    wait_vmcnt<(S - 2) * kLoadsPerWave>();
+    __syncthreads();
+    {
+      const int nxt = it + S - 1;
+      issue(nxt < nk ? nxt : nk, nxt % S);
+    }
+    const char* la = smem + (it % S) * kStage;
+    const char* lb = la + TA::kBytes;
+    const char* lsa = la + kScaleOff;
+    const char* lsb = lsa + TA::kScaleBytes;
+    uint32_t sca[TM], scb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sca[i] = TA::scales(lsa, wm * WM + i * 32, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) scb[j] = TB::scales(lsb, wn * WN + j * 32, lane);
+#pragma unroll
+    for (int ks = 0; ks < kF8RowBytes / 64; ++ks) {
+      const int sh = 8 * (2 * ks + (lane >> 5));
+      i32x8 fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[i] = TA::frag(la, wm * WM + i * 32, ks, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = TB::frag(lb, wn * WN + j * 32, ks, lane);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[i], fb[j], acc[i][j], 0, 0, 0, int((sca[i] >> sh) & 0xFFu), 0, int((scb[j] >> sh) & 0xFFu));
+    }
+  }
+  wait_vmcnt<0>();
+
+  const int rib = 4 * (lane >> 5), cib = lane & 31;
+  const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
+  __bf16* C = static_cast<__bf16*>(g.c);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + wn * WN + j * 32 + cib;
+      const int mb = m0 + wm * WM + i * 32 + rib;
+      if (interior) {
+        __bf16* p = C + int64_t(mb) * g.ldc + n;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[int64_t(8 * (r >> 2) + (r & 3)) * g.ldc] = static_cast<__bf16>(acc[i][j][r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = mb + 8 * (r >> 2) + (r & 3);
+          if (m < g.M && n < g.N) C[int64_t(m) * g.ldc + n] = static_cast<__bf16>(acc[i][j][r]);
+        }
+      }
+    }
+}
+
+// bf16 out[r][c] = E4M3(codes[r][c]) * 2^(scales[r][c/32] - 127), 16 elements per thread.
+__global__ void mx_dequant_bf16(const uint8_t* codes, const uint8_t* scales, uint16_t* out, int64_t rows,
+                                int64_t cols) {
+  const int64_t n16 = rows * (cols / 16);
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    const int64_t r = i / (cols / 16), c = (i % (cols / 16)) * 16;
+    const uint4 q = *reinterpret_cast<const uint4*>(codes + r * cols + c);
+    const uint32_t s = scales[r * (cols / 32) + c / 32];
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const uint32_t src = w[h >> 1];
+      const int sh = (h & 1) * 16;
+      o[h] = e4m3_to_bf16((src >> sh) & 0xFFu, s) | (e4m3_to_bf16((src >> (sh + 8)) & 0xFFu, s) << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(out + r * cols + c);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+template <int BM, int BN, int S, int WGM, int WGN>
+int launch_f8(hipStream_t st, F8Args g) {
+  constexpr int lds = S * (F8Tile<BM>::kBytes + F8Tile<BN>::kBytes +
+                           ((F8Tile<BM>::kScaleBytes + F8Tile<BN>::kScaleBytes + 255) / 256) * 256 + 256);
+  auto kfn = gemm_f8fwd<BM, BN, S, WGM, WGN>;
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+      return -5;
+    attr = true;
+  }
+  g.tiles_m = (g.M + BM - 1) / BM;
+  g.tiles_n = (g.N + BN - 1) / BN;
+  hipLaunchKernelGGL(kfn, dim3(g.tiles_m * g.tiles_n), dim3(WGM * WGN * 64), lds, st, g);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+}  // namespace sl2
+
+int f8_fwd(hipStream_t st, F8Args g) {
+  switch (g.cfg) {
+    case 0: return sl2::launch_f8<256, 256, 2, 2, 4>(st, g);
+    case 1: return sl2::launch_f8<128, 128, 3, 2, 2>(st, g);
+    default: return -1;
+  }
+}
+
+int mx_dequant(hipStream_t st, const uint8_t* codes, const uint8_t* scales, void* out, int64_t rows, int64_t cols) {
+  const int64_t n16 = rows * (cols / 16);
+  if (n16 == 0) return 0;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(sl2::mx_dequant_bf16, dim3(unsigned(blocks)), dim3(256), 0, st, codes, scales,
+                     static_cast<uint16_t*>(out), rows, cols);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}

@@ -85,11 +85,8 @@ _WS = {}
 
 
 def wgrad_workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
-    """A zero-initialised workspace of at least ``nbytes`` for the current stream of ``dev``.
-
-    The kernels return the workspace's counters to zero after every call, so one buffer per
-    stream is reused; it only grows (a fresh zero buffer) when a larger size is asked for.
-    """
+    """A workspace of at least ``nbytes`` for the current stream of ``dev`` (contents never
+    matter to the kernels); one buffer per stream is reused and only grows."""
     key = (dev, torch.cuda.current_stream(dev).cuda_stream)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
@@ -133,7 +130,11 @@ def sl_linear_fwd_mxfp8(Xq, Xs, Wq, Ws, Y=None):
     return Y
 
 
-def sl_linear_dgrad_mxfp8w(dY, Wq, Ws, dX=None):
+def sl_mxfp8_workspace_bytes(T: int, n_in: int, n_out: int) -> int:
+    return int(lib().sl_mxfp8_workspace_bytes(T, n_in, n_out))
+
+
+def sl_linear_dgrad_mxfp8w(dY, Wq, Ws, dX=None, workspace=None):
     """dX = dY . deq(Wq, Ws) (bf16 in/out)."""
     dev = _device(dY)
     T, n_out = dY.shape
@@ -144,8 +145,12 @@ def sl_linear_dgrad_mxfp8w(dY, Wq, Ws, dX=None):
     if dX is None:
         dX = torch.empty((T, n_in), dtype=BF16, device=dev)
     _want(dX, "dX", BF16, (T, n_in), dev)
+    need = sl_mxfp8_workspace_bytes(T, n_in, n_out)
+    if workspace is None:
+        workspace = wgrad_workspace(dev, need) if need else None
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check("sl_linear_dgrad_mxfp8w", lib().sl_linear_dgrad_mxfp8w(
-        _stream(dev), _ptr(dY), _ptr(Wq), _ptr(Ws), _ptr(dX), T, n_in, n_out))
+        _stream(dev), _ptr(dY), _ptr(Wq), _ptr(Ws), _ptr(dX), T, n_in, n_out, _ptr(workspace), nbytes))
     return dX
 
 
@@ -158,7 +163,7 @@ def sl_linear_wgrad_accum_mxfp8x(Xq, Xs, dY, main_grad, workspace=None):
     _want(Xs, "Xs", U8, (T, n_in // 32), dev)
     _want(dY, "dY", BF16, (T, n_out), dev)
     _want(main_grad, "main_grad", F32, (n_out, n_in), dev)
-    need = sl_wgrad_workspace_bytes(T, n_in, n_out)
+    need = sl_mxfp8_workspace_bytes(T, n_in, n_out)
     if workspace is None:
         workspace = wgrad_workspace(dev, need) if need else None
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

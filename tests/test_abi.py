@@ -80,7 +80,12 @@ def test_wgrad_validation():
 def test_mxfp8_validation():
     L = _lib.lib()
     assert L.sl_linear_fwd_mxfp8(None, A, A, A, A, A, 16, 48, 16) == SL_ESHAPE     # in % 32
-    assert L.sl_linear_dgrad_mxfp8w(None, A, A, A, A, 16, 48, 16) == SL_ESHAPE
+    assert L.sl_linear_dgrad_mxfp8w(None, A, A, A, A, 16, 48, 16, None, 0) == SL_ESHAPE
+    need = L.sl_mxfp8_workspace_bytes(8192, 2048, 8192)
+    assert need >= 8192 * 2048 * 2                                           # dequantised operand
+    assert L.sl_linear_dgrad_mxfp8w(None, A, A, A, A, 8192, 2048, 8192, None, 0) == SL_EWORKSPACE
+    assert L.sl_linear_wgrad_accum_mxfp8x(None, A, A, A, A, 8192, 2048, 8192, A, 1024) == SL_EWORKSPACE
+    assert L.sl_mxfp8_workspace_bytes(0, 64, 64) == 0 and L.sl_mxfp8_workspace_bytes(8, 48, 8) == 0
     assert L.sl_linear_wgrad_accum_mxfp8x(None, A, A, A, A, 16, 48, 16, None, 0) == SL_ESHAPE
     assert L.sl_linear_fwd_mxfp8(None, A, None, A, A, A, 16, 64, 16) == SL_EINVAL   # no scales
     assert L.sl_linear_fwd_mxfp8(None, MIS, A, A, A, A, 16, 64, 16) == SL_EALIGN

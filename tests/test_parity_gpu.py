@@ -246,7 +246,8 @@ def test_autograd_glue():
 # MXFP8 operand variants
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("T,n_in,n_out", [(1, 32, 8), (300, 288, 520), (4104, 256, 520), (4100, 288, 3336)])
+@pytest.mark.parametrize("T,n_in,n_out", [(1, 32, 8), (300, 288, 520), (4104, 256, 520), (4100, 288, 3336),
+                                          (1000, 384, 776), (4100, 512, 3336)])
 def test_mxfp8_elementwise(T, n_in, n_out):
     say(f"case mxfp8 T={T} in={n_in} out={n_out}")
     Xq, Xs = synth.mxfp8_normal((T, n_in), 21)
@@ -265,17 +266,20 @@ def test_mxfp8_elementwise(T, n_in, n_out):
     assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
 
 
-def test_mxfp8_all_codes_decode_exactly():
-    """Every finite E4M3 code under several scales: a one-hot fwd returns the decoded value."""
-    say("case mxfp8 decode table")
+@pytest.mark.parametrize("n_in", [32, 128])
+def test_mxfp8_all_codes_decode_exactly(n_in):
+    """Every finite E4M3 code under several scales: a one-hot fwd returns the decoded value
+    (in = 32: register-dequantising kernel; in = 128: block-scaled fp8 MFMA)."""
+    say(f"case mxfp8 decode table in={n_in}")
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)   # 254 codes
     n_out = 256
-    Wq = np.zeros((n_out, 32), np.uint8)
-    Wq[: codes.size, 0] = codes
+    Wq = np.zeros((n_out, n_in), np.uint8)
+    Wq[: codes.size, n_in - 1] = codes                                               # last block
     for s in (100, 120, 127, 135):
-        Ws = np.full((n_out, 1), s, np.uint8)
-        Xq = np.zeros((1, 32), np.uint8); Xq[0, 0] = 0x38                            # 1.0
-        Xs = np.full((1, 1), 127, np.uint8)
+        Ws = np.full((n_out, n_in // 32), 127, np.uint8)
+        Ws[:, -1] = s
+        Xq = np.zeros((1, n_in), np.uint8); Xq[0, n_in - 1] = 0x38                   # 1.0
+        Xs = np.full((1, n_in // 32), 127, np.uint8)
         Y = host_f64(sl.sl_linear_fwd_mxfp8(dev_u8(Xq), dev_u8(Xs), dev_u8(Wq), dev_u8(Ws)))[0]
         want = ol.linear_fwd_mxfp8(Xq, Xs, Wq, Ws)[0]
         assert np.array_equal(Y, want), s
