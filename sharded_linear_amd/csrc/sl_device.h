@@ -7,6 +7,7 @@
 namespace sl2 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -27,6 +28,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+
+// s_waitcnt lgkmcnt(0) with vmcnt and expcnt unconstrained: this wave's LDS reads are complete.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Raw buffer descriptor over one operand (gfx9 layout: base, stride 0, num_records = byte
 // extent, format word).  Offsets outside the extent -- including kOOB, above every extent the
@@ -50,6 +54,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // the kernel orders these loads itself with wait_vmcnt<>() and a barrier.
 __device__ __forceinline__ void lds_dma16(i32x4 rs, uint32_t lds, uint32_t voff) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rs), "{m0}"(lds) : "memory");
+}
+
+// As lds_dma16, with a wave-uniform byte offset `soff` added to the address.  Lanes whose voff
+// lies past the descriptor's extent still read zeros, and in-range lanes must stay in range
+// with soff added (the caller only uses it that way), so the result does not depend on whether
+// the range check includes soff.
+__device__ __forceinline__ void lds_dma16s(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds) : "memory");
 }
 
 // One 4-byte-per-lane HBM->LDS load: lane i writes LDS [lds + 4 i, +4).

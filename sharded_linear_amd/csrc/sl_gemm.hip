@@ -407,7 +407,7 @@ Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a
     if (cfg < 0) {
       // 8-wave 256x256 tiles wherever they fill the chip (and always for the weight gradient,
       // which splits K instead); otherwise 256x128 / 128x256, else 128x128.
-      if (ntiles(M, N, 256, 256) >= 200 || kind == Kind::Wgrad) cfg = kind == Kind::Fwd ? 6 : 10;
+      if (ntiles(M, N, 256, 256) >= 200 || kind == Kind::Wgrad) cfg = 10;
       else if (ntiles(M, N, 256, 128) >= 200) cfg = M >= N ? 3 : 4;
       else cfg = 2;
     }

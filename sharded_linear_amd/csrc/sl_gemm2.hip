@@ -14,8 +14,8 @@
 //    source lane 4j+q, element e.  Source lane 4j+q reads 4 consecutive free indices at k row
 //    kb+j, so every result lane holds 4 consecutive k of one free index -- the MFMA layout.
 //
-// MFMA: v_mfma_f32_32x32x16_bf16 (lane l: row/column l%32, k = 8*(l/32)+0..7; result lane l
-// holds column l%32, rows 8*(r/4) + 4*(l/32) + r%4).
+// MFMA: v_mfma_f32_32x32x16_bf16 (operand lane l: row/column l%32, k = 8*(l/32)+0..7; result
+// lane l holds column l%32, rows 8*(r/4) + 4*(l/32) + r%4).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -57,6 +57,18 @@ struct KMaj {
       lds_dma16(rs, lds_addr(lds + wl * 1024), off);
     }
   }
+  // Byte offsets of this thread's loads relative to the stage's first k (rows outside the matrix
+  // -> kOOB).  A stage wholly inside K then loads with these and a scalar offset of 2 k0.
+  template <int WAVES, int N = kLoads / WAVES>
+  __device__ static __forceinline__ void prep(uint32_t (&voff)[N], int lane, int wave, int row0, int rows,
+                                              int64_t ld) {
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int p = (it * WAVES + wave) * 64 + lane;
+      const int r = p / kCPR, c = (p % kCPR) ^ swz(p / kCPR);
+      voff[it] = row0 + r < rows ? uint32_t((int64_t(row0 + r) * ld + c * 8) * 2) : kOOB;
+    }
+  }
   // fragment of 32 rows starting at r0, k16 step ks: lane l gets row r0 + l%32, k 8(l/32)..+7
   __device__ static __forceinline__ bf16x8 frag(const char* lds, int r0, int ks, int lane) {
     const int r = r0 + (lane & 31);
@@ -92,6 +104,19 @@ struct MNMaj {
       lds_dma16(rs, lds_addr(lds + wl * 1024), off);
     }
   }
+  // Byte offsets relative to the stage's first k row (columns outside the matrix -> kOOB); a
+  // stage wholly inside K loads with these and a scalar offset of 2 k0 ld.
+  template <int WAVES, int N = kLoads / WAVES>
+  __device__ static __forceinline__ void prep(uint32_t (&voff)[N], int lane, int wave, int col0, int cols,
+                                              int64_t ld) {
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int p = (it * WAVES + wave) * 64 + lane;
+      const int k = p / kCPR, c = (p % kCPR) ^ swz(p / kCPR);
+      const int gc = col0 + c * 8;
+      voff[it] = gc < cols ? uint32_t((int64_t(k) * ld + gc) * 2) : kOOB;
+    }
+  }
   // fragment of 32 free indices from f0, k16 step ks, via two transposing reads
   __device__ static __forceinline__ bf16x8 frag(const char* lds, int f0, int ks, int lane) {
     const int g = lane >> 4, s = lane & 15, j = s >> 2, q = s & 3;
@@ -124,6 +149,105 @@ struct OpSel { using T = KMaj<R, BK>; };
 template <int R, int BK>
 struct OpSel<false, R, BK> { using T = MNMaj<R, BK>; };
 
+// Workgroup -> macro-tile: blocks are dealt round-robin to the XCDs, so the block id is first
+// remapped to make each XCD's blocks a contiguous run of tile ids; tile ids then walk groups of
+// 8 tile rows column by column, so the tiles one XCD runs at a time share A and B panels in its L2.
+template <int BM, int BN>
+__device__ __forceinline__ void tile_origin(const Gemm2Args& g, int& m0, int& n0) {
+  const int ntiles = g.tiles_m * g.tiles_n;
+  const int t = xcd_remap(blockIdx.x, ntiles);
+  const int group = t / (8 * g.tiles_n);
+  const int first_m = group * 8;
+  const int gsz = min(g.tiles_m - first_m, 8);
+  const int tm = first_m + (t % (8 * g.tiles_n)) % gsz;
+  const int tn = (t % (8 * g.tiles_n)) / gsz;
+  m0 = tm * BM;
+  n0 = tn * BN;
+}
+
+// Loads [LO, HI) of one stage of an operand with precomputed offsets (wave `w` issues wave-loads
+// it * WAVES + w, each 1 KiB of LDS).
+// `koff` is the stage's byte offset along k, applied through the instruction's scalar offset.
+template <int WAVES, int LO, int HI, int N>
+__device__ __forceinline__ void load_pre(i32x4 rs, char* lds, int wave, const uint32_t (&voff)[N], uint32_t koff) {
+#pragma unroll
+  for (int it = LO; it < HI; ++it) lds_dma16s(rs, lds_addr(lds + (it * WAVES + wave) * 1024), voff[it], koff);
+}
+
+// ---- epilogue -------------------------------------------------------------------------------
+// The MFMAs take the B fragment as their first operand, so block (i, j) of a wave holds C^T:
+// lane l has row 32 i + l%32 of the wave tile, and registers 4q..4q+3 hold its four consecutive
+// columns 32 j + 8q + 4(l/32) + 0..3.  Each group of 32 rows goes through the wave's own LDS
+// region (the operand ring is idle by then): lanes write their 4-column pieces, then read back
+// whole 16-byte row chunks, so every global access is 16 bytes per lane along a row.  16-byte
+// chunks are XOR-swizzled by row, which keeps both the column-piece writes and the row reads free
+// of bank conflicts.  Since M-edge rows and N (a multiple of 8) cut only whole chunks, edge tiles
+// need one predicate per chunk.
+template <int WN, bool ACC>
+struct Epi {
+  static constexpr int kES = ACC ? 4 : 2;               // bytes per element
+  static constexpr int kRowBytes = WN * kES;
+  static constexpr int kCPR = kRowBytes / 16;           // 16-byte chunks per row
+  static constexpr int kRPI = 64 / kCPR;                // rows per wave instruction
+  static constexpr int kBytes = 32 * kRowBytes;         // LDS per wave
+  __device__ static __forceinline__ int off(int r, int c) { return r * kRowBytes + ((c ^ (r & (kCPR - 1))) << 4); }
+};
+
+template <int BM, int BN, int WN, int TM, int TN, bool ACC>
+__device__ __forceinline__ void store_tile(const Gemm2Args& g, f32x16 (&acc)[TM][TN], char* smem, int mw, int nw,
+                                           int split, int lane, int wave) {
+  using E = Epi<WN, ACC>;
+  char* ep = smem + wave * E::kBytes;
+  const int rl = lane & 31, hl = lane >> 5;
+  const int rr = lane / E::kCPR, cr = lane % E::kCPR;    // read-back: row within an instruction, chunk
+  float* Cf = nullptr;
+  int64_t ldc = g.ldc;
+  bool direct = true;
+  if constexpr (ACC) {
+    direct = g.splits == 1;
+    Cf = direct ? static_cast<float*>(g.c) : g.ws + int64_t(split) * g.M * g.N;
+    if (!direct) ldc = g.N;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = j * 32 + 8 * q + 4 * hl;
+        if constexpr (ACC) {
+          *reinterpret_cast<float4*>(ep + E::off(rl, col / 4)) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        } else {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(acc[i][j][4 * q + e]);
+          *reinterpret_cast<bf16x4*>(ep + E::off(rl, col / 8) + 8 * hl) = v;
+        }
+      }
+#pragma unroll
+    for (int t = 0; t < 32 / E::kRPI; ++t) {
+      const int r = t * E::kRPI + rr;
+      const int m = mw + i * 32 + r;
+      const int n = nw + cr * (16 / E::kES);
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + E::off(r, cr));
+      if (m < g.M && n < g.N) {
+        if constexpr (ACC) {
+          float4* p = reinterpret_cast<float4*>(Cf + int64_t(m) * ldc + n);
+          float4 x = __builtin_bit_cast(float4, v);
+          if (direct) {
+            const float4 o = *p;
+            x = make_float4(o.x + x.x, o.y + x.y, o.z + x.z, o.w + x.w);
+          }
+          *p = x;
+        } else {
+          *reinterpret_cast<uint4*>(static_cast<__bf16*>(g.c) + int64_t(m) * g.ldc + n) = v;
+        }
+      }
+    }
+  }
+}
+
 // SCHED 0 leaves instruction order to the compiler; SCHED 1 asks it (sched_group_barrier) to
 // alternate MFMAs with the LDS fragment reads of the next k16 step.
 template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED, int OCC>
@@ -141,14 +265,8 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
 
-  const int ntiles = g.tiles_m * g.tiles_n;
-  const int t = xcd_remap(blockIdx.x, ntiles);
-  const int group = t / (8 * g.tiles_n);
-  const int first_m = group * 8;
-  const int gsz = min(g.tiles_m - first_m, 8);
-  const int tm = first_m + (t % (8 * g.tiles_n)) % gsz;
-  const int tn = (t % (8 * g.tiles_n)) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
+  int m0, n0;
+  tile_origin<BM, BN>(g, m0, n0);
 
   const int split = blockIdx.z;
   const int nkt = (g.K + BK - 1) / BK;
@@ -158,26 +276,29 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
 
   const i32x4 ra = rsrc(g.a, g.a_bytes), rb = rsrc(g.b, g.b_bytes);
 
-  auto issue = [&](int kt, int slot) {
-    char* base = smem + slot * kStage;
-    const int k0 = kt * BK;
-    OA::template load<WAVES>(ra, base, lane, wave, m0, g.M, k0, g.K, g.lda);
-    OB::template load<WAVES>(rb, base + OA::kBytes, lane, wave, n0, g.N, k0, g.K, g.ldb);
-  };
   // The loads of one stage, split into BK/16 parts issued one per k16 step of the loop.
   constexpr int NP = BK / 16;
   constexpr int LA = OA::kLoads / WAVES, LB = OB::kLoads / WAVES;
   constexpr bool kSpread = LA % NP == 0 && LB % NP == 0;
+  // Stages wholly inside K use offsets computed once plus a scalar offset for the stage's first k
+  // (no vector work per load); a ragged last stage checks k per load.
+  uint32_t voa[LA], vob[LB];
+  OA::template prep<WAVES>(voa, lane, wave, m0, g.M, g.lda);
+  OB::template prep<WAVES>(vob, lane, wave, n0, g.N, g.ldb);
   auto issue_part = [&](int kt, int slot, auto part) {
     constexpr int P = decltype(part)::value;
-    char* base = smem + slot * kStage;
-    const int k0 = kt * BK;
-    if constexpr (kSpread) {
-      OA::template load<WAVES, P * LA / NP, (P + 1) * LA / NP>(ra, base, lane, wave, m0, g.M, k0, g.K, g.lda);
-      OB::template load<WAVES, P * LB / NP, (P + 1) * LB / NP>(rb, base + OA::kBytes, lane, wave, n0, g.N, k0, g.K, g.ldb);
-    } else if constexpr (P == 0) {
-      OA::template load<WAVES>(ra, base, lane, wave, m0, g.M, k0, g.K, g.lda);
-      OB::template load<WAVES>(rb, base + OA::kBytes, lane, wave, n0, g.N, k0, g.K, g.ldb);
+    constexpr int A0 = kSpread ? P * LA / NP : 0, A1 = kSpread ? (P + 1) * LA / NP : LA;
+    constexpr int B0 = kSpread ? P * LB / NP : 0, B1 = kSpread ? (P + 1) * LB / NP : LB;
+    if constexpr (kSpread || P == 0) {
+      char* base = smem + slot * kStage;
+      const int k0 = kt * BK;
+      if (k0 + BK <= g.K) {
+        load_pre<WAVES, A0, A1>(ra, base, wave, voa, uint32_t(A_KM ? int64_t(k0) * 2 : int64_t(k0) * g.lda * 2));
+        load_pre<WAVES, B0, B1>(rb, base + OA::kBytes, wave, vob, uint32_t(B_KM ? int64_t(k0) * 2 : int64_t(k0) * g.ldb * 2));
+      } else {
+        OA::template load<WAVES, A0, A1>(ra, base, lane, wave, m0, g.M, k0, g.K, g.lda);
+        OB::template load<WAVES, B0, B1>(rb, base + OA::kBytes, lane, wave, n0, g.N, k0, g.K, g.ldb);
+      }
     }
   };
 
@@ -191,7 +312,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
 
   // prologue: S-1 stages in flight (stages past the end load zeros: uniform wait counts)
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(kt0 + (s < nk ? s : nk), s);
+  for (int s = 0; s < S - 1; ++s) static_for<NP>([&](auto pc) { issue_part(kt0 + (s < nk ? s : nk), s, pc); });
 
   for (int it = 0; it < nk; ++it) {
     wait_vmcnt<(S - 2) * kLoadsPerThread>();
@@ -221,7 +342,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
       if constexpr (SCHED == 1 && ks + 1 < NP) {
         constexpr int kDs = TM * (A_KM ? 1 : 2) + TN * (B_KM ? 1 : 2);
 #pragma unroll
@@ -235,75 +356,17 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
   }
   wait_vmcnt<0>();
 
-  // ---- epilogue ----------------------------------------------------------------------------
-  // Lane l holds column l%32 of each 32x32 block, rows 8*(r/4) + 4*(l/32) + r%4.  Tiles fully
-  // inside the matrix take a branch-free path (loads of a block batched before its adds).
-  const int rib = 4 * (lane >> 5), cib = lane & 31;
-  const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
-  if constexpr (!ACC) {
-    __bf16* C = static_cast<__bf16*>(g.c);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 32 + cib;
-        const int mb = m0 + wm * WM + i * 32 + rib;
-        if (interior) {
-          __bf16* p = C + int64_t(mb) * g.ldc + n;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) p[int64_t(8 * (r >> 2) + (r & 3)) * g.ldc] = static_cast<__bf16>(acc[i][j][r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = mb + 8 * (r >> 2) + (r & 3);
-            if (m < g.M && n < g.N) C[int64_t(m) * g.ldc + n] = static_cast<__bf16>(acc[i][j][r]);
-          }
-        }
-      }
-  } else {
-    // Unsplit: the single fp32 read-modify-write of main_grad.  Split-K: this split's partial
-    // goes to its own plane ws[split][M][N] with plain stores; the reduce kernel launched next
-    // on the stream adds the planes in split order into main_grad.
-    const bool direct = g.splits == 1;
-    float* C = direct ? static_cast<float*>(g.c) : g.ws + int64_t(split) * g.M * g.N;
-    const int64_t ldc = direct ? g.ldc : g.N;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 32 + cib;
-        const int mb = m0 + wm * WM + i * 32 + rib;
-        if (interior) {
-          float* p = C + int64_t(mb) * ldc + n;
-          if (direct) {
-            float old[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) old[r] = p[int64_t(8 * (r >> 2) + (r & 3)) * ldc];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) p[int64_t(8 * (r >> 2) + (r & 3)) * ldc] = old[r] + acc[i][j][r];
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) p[int64_t(8 * (r >> 2) + (r & 3)) * ldc] = acc[i][j][r];
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = mb + 8 * (r >> 2) + (r & 3);
-            if (m < g.M && n < g.N) {
-              float* p = C + int64_t(m) * ldc + n;
-              *p = direct ? *p + acc[i][j][r] : acc[i][j][r];
-            }
-          }
-        }
-      }
-  }
+  __syncthreads();    // every wave is past its last operand read: the ring becomes epilogue space
+  store_tile<BM, BN, WN, TM, TN, ACC>(g, acc, smem, m0 + wm * WM, n0 + wn * WN, split, lane, wave);
 }
 
 template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED = 0, int OCC = 1>
 int launch_cfg(hipStream_t st, Gemm2Args g) {
   using OA = typename OpSel<A_KM, BM, BK>::T;
   using OB = typename OpSel<B_KM, BN, BK>::T;
-  constexpr int lds = S * (OA::kBytes + OB::kBytes);
+  constexpr int ring = S * (OA::kBytes + OB::kBytes);
+  constexpr int epi = WGM * WGN * Epi<BN / WGN, ACC>::kBytes;
+  constexpr int lds = ring > epi ? ring : epi;
   auto kfn = gemm2<BM, BN, BK, S, WGM, WGN, A_KM, B_KM, ACC, SCHED, OCC>;
   static bool attr = false;
   if (!attr) {
@@ -362,9 +425,10 @@ int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) 
 
 void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
   *bk = (cfg == 0 || cfg == 7 || cfg == 8 || cfg >= 12) ? 32 : 64;
-  static const int t[15][2] = {{256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256},
-                               {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256},
-                               {256, 128}, {128, 256}, {256, 128}};
+  static const int t[kGemm2Configs][2] = {
+      {256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256}, {256, 256},
+      {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {128, 256},
+      {256, 128}};
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }
