@@ -399,18 +399,30 @@ int splits_override() {
   return (v >= 1 && v <= 64) ? v : 0;
 }
 
+// Tile configuration for a forward / dgrad GEMM: each candidate's time is estimated as the number
+// of rounds of workgroups over the 256 CUs times one round's work (tile area x workgroups per CU)
+// over the candidate's measured efficiency relative to the 8-wave 256x256 kernel.  The weight
+// gradient always takes 256x256 tiles and fills the chip by splitting K instead.
+int pick_config(int64_t M, int64_t N) {
+  struct Cand { int cfg, bm, bn, occ; double eff; };
+  static const Cand cand[] = {{10, 256, 256, 1, 1.0}, {12, 256, 128, 2, 0.85}, {13, 128, 256, 2, 0.85},
+                              {3, 256, 128, 1, 0.78}, {4, 128, 256, 1, 0.78}, {2, 128, 128, 1, 0.6}};
+  int best = 10;
+  double best_t = 0.0;
+  for (const Cand& c : cand) {
+    const int64_t rounds = (ntiles(M, N, c.bm, c.bn) + 256 * c.occ - 1) / (256 * c.occ);
+    const double t = double(rounds) * double(c.bm * c.bn * c.occ) / c.eff;
+    if (best_t == 0.0 || t < best_t) { best = c.cfg; best_t = t; }
+  }
+  return best;
+}
+
 Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a_bytes, int64_t b_bytes) {
   Plan p{};
   p.v2 = !mxfp8 && a_bytes <= kMaxDmaBytes && b_bytes <= kMaxDmaBytes;
   if (p.v2) {
     int cfg = config_override(kind);
-    if (cfg < 0) {
-      // 8-wave 256x256 tiles wherever they fill the chip (and always for the weight gradient,
-      // which splits K instead); otherwise 256x128 / 128x256, else 128x128.
-      if (ntiles(M, N, 256, 256) >= 200 || kind == Kind::Wgrad) cfg = 10;
-      else if (ntiles(M, N, 256, 128) >= 200) cfg = M >= N ? 3 : 4;
-      else cfg = 2;
-    }
+    if (cfg < 0) cfg = kind == Kind::Wgrad ? 10 : pick_config(M, N);
     p.cfg = cfg;
     gemm2_tile(cfg, &p.bm, &p.bn, &p.bk);
   } else {

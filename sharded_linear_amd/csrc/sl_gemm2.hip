@@ -177,71 +177,95 @@ __device__ __forceinline__ void load_pre(i32x4 rs, char* lds, int wave, const ui
 // ---- epilogue -------------------------------------------------------------------------------
 // The MFMAs take the B fragment as their first operand, so block (i, j) of a wave holds C^T:
 // lane l has row 32 i + l%32 of the wave tile, and registers 4q..4q+3 hold its four consecutive
-// columns 32 j + 8q + 4(l/32) + 0..3.  Each group of 32 rows goes through the wave's own LDS
-// region (the operand ring is idle by then): lanes write their 4-column pieces, then read back
-// whole 16-byte row chunks, so every global access is 16 bytes per lane along a row.  16-byte
-// chunks are XOR-swizzled by row, which keeps both the column-piece writes and the row reads free
-// of bank conflicts.  Since M-edge rows and N (a multiple of 8) cut only whole chunks, edge tiles
-// need one predicate per chunk.
-template <int WN, bool ACC>
+// columns 32 j + 8q + 4(l/32) + 0..3.  Results go through the wave's own LDS region (the operand
+// ring is idle by then): lanes write their 4-column pieces, then read back whole 16-byte row
+// chunks, so every global access is 16 bytes per lane along a row.  16-byte chunks are
+// XOR-swizzled by row, which keeps the row reads and most column-piece writes free of bank
+// conflicts.  M-edge rows and N (a multiple of 8) cut only whole chunks, so edge tiles need one
+// predicate per chunk.  bf16 results stage the whole wave tile at once; fp32 results go 32 rows
+// at a time, with the old main_grad values of the next 32 rows loaded while the current ones
+// are staged (or, for wide wave tiles, the current rows' values loaded before their staging).
+template <int WN, int ROWS, bool ACC>
 struct Epi {
   static constexpr int kES = ACC ? 4 : 2;               // bytes per element
   static constexpr int kRowBytes = WN * kES;
   static constexpr int kCPR = kRowBytes / 16;           // 16-byte chunks per row
   static constexpr int kRPI = 64 / kCPR;                // rows per wave instruction
-  static constexpr int kBytes = 32 * kRowBytes;         // LDS per wave
+  static constexpr int kBytes = ROWS * kRowBytes;       // LDS per wave
   __device__ static __forceinline__ int off(int r, int c) { return r * kRowBytes + ((c ^ (r & (kCPR - 1))) << 4); }
 };
+template <int WM, int WN, bool ACC>
+using EpiOf = Epi<WN, ACC ? 32 : WM, ACC>;
 
-template <int BM, int BN, int WN, int TM, int TN, bool ACC>
+template <int WM, int WN, int TM, int TN, bool ACC>
 __device__ __forceinline__ void store_tile(const Gemm2Args& g, f32x16 (&acc)[TM][TN], char* smem, int mw, int nw,
                                            int split, int lane, int wave) {
-  using E = Epi<WN, ACC>;
+  using E = EpiOf<WM, WN, ACC>;
   char* ep = smem + wave * E::kBytes;
   const int rl = lane & 31, hl = lane >> 5;
   const int rr = lane / E::kCPR, cr = lane % E::kCPR;    // read-back: row within an instruction, chunk
-  float* Cf = nullptr;
-  int64_t ldc = g.ldc;
-  bool direct = true;
-  if constexpr (ACC) {
-    direct = g.splits == 1;
-    Cf = direct ? static_cast<float*>(g.c) : g.ws + int64_t(split) * g.M * g.N;
-    if (!direct) ldc = g.N;
-  }
+  const int n = nw + cr * (16 / E::kES);
+  if constexpr (!ACC) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = j * 32 + 8 * q + 4 * hl;
-        if constexpr (ACC) {
-          *reinterpret_cast<float4*>(ep + E::off(rl, col / 4)) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        } else {
+        for (int q = 0; q < 4; ++q) {
           bf16x4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(acc[i][j][4 * q + e]);
-          *reinterpret_cast<bf16x4*>(ep + E::off(rl, col / 8) + 8 * hl) = v;
+          *reinterpret_cast<bf16x4*>(ep + E::off(i * 32 + rl, (j * 32 + 8 * q) / 8) + 8 * hl) = v;
         }
+    __bf16* C = static_cast<__bf16*>(g.c);
+#pragma unroll
+    for (int t = 0; t < WM / E::kRPI; ++t) {
+      const int r = t * E::kRPI + rr, m = mw + r;
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + E::off(r, cr));
+      if (m < g.M && n < g.N) *reinterpret_cast<uint4*>(C + int64_t(m) * g.ldc + n) = v;
+    }
+  } else {
+    // Unsplit: the single fp32 read-modify-write of main_grad.  Split-K: this split's partial
+    // goes to its own plane ws[split][M][N] with plain stores; the reduce kernel launched next
+    // on the stream adds the planes in split order into main_grad.
+    constexpr int RI = 32 / E::kRPI;
+    const bool direct = g.splits == 1;
+    float* C = direct ? static_cast<float*>(g.c) : g.ws + int64_t(split) * g.M * g.N;
+    const int64_t ldc = direct ? g.ldc : g.N;
+    constexpr int NB = RI <= 8 ? 2 : 1;   // double-buffer the old values when registers allow
+    float4 old[NB][RI];
+    auto load_old = [&](int i, float4 (&o)[RI]) {
+#pragma unroll
+      for (int t = 0; t < RI; ++t) {
+        const int m = mw + i * 32 + t * E::kRPI + rr;
+        o[t] = (m < g.M && n < g.N) ? *reinterpret_cast<const float4*>(C + int64_t(m) * ldc + n)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    if (direct && NB == 2) load_old(0, old[0]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if constexpr (NB == 2) {
+        if (direct && i + 1 < TM) load_old(i + 1, old[(i + 1) & 1]);
+      } else {
+        if (direct) load_old(i, old[0]);
       }
 #pragma unroll
-    for (int t = 0; t < 32 / E::kRPI; ++t) {
-      const int r = t * E::kRPI + rr;
-      const int m = mw + i * 32 + r;
-      const int n = nw + cr * (16 / E::kES);
-      const uint4 v = *reinterpret_cast<const uint4*>(ep + E::off(r, cr));
-      if (m < g.M && n < g.N) {
-        if constexpr (ACC) {
-          float4* p = reinterpret_cast<float4*>(Cf + int64_t(m) * ldc + n);
-          float4 x = __builtin_bit_cast(float4, v);
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(ep + E::off(rl, (j * 32 + 8 * q + 4 * hl) / 4)) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+#pragma unroll
+      for (int t = 0; t < RI; ++t) {
+        const int r = t * E::kRPI + rr, m = mw + i * 32 + r;
+        float4 x = *reinterpret_cast<const float4*>(ep + E::off(r, cr));
+        if (m < g.M && n < g.N) {
           if (direct) {
-            const float4 o = *p;
+            const float4 o = old[i % NB][t];
             x = make_float4(o.x + x.x, o.y + x.y, o.z + x.z, o.w + x.w);
           }
-          *p = x;
-        } else {
-          *reinterpret_cast<uint4*>(static_cast<__bf16*>(g.c) + int64_t(m) * g.ldc + n) = v;
+          *reinterpret_cast<float4*>(C + int64_t(m) * ldc + n) = x;
         }
       }
     }
@@ -249,7 +273,8 @@ __device__ __forceinline__ void store_tile(const Gemm2Args& g, f32x16 (&acc)[TM]
 }
 
 // SCHED 0 leaves instruction order to the compiler; SCHED 1 asks it (sched_group_barrier) to
-// alternate MFMAs with the LDS fragment reads of the next k16 step.
+// alternate MFMAs with the LDS fragment reads of the next k16 step; SCHED 2 does the same and
+// moves the stage barrier into the last k16 step (see the loop).
 template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED, int OCC>
 __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
   constexpr int WAVES = WGM * WGN;
@@ -279,17 +304,17 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
   // The loads of one stage, split into BK/16 parts issued one per k16 step of the loop.
   constexpr int NP = BK / 16;
   constexpr int LA = OA::kLoads / WAVES, LB = OB::kLoads / WAVES;
-  constexpr bool kSpread = LA % NP == 0 && LB % NP == 0;
   // Stages wholly inside K use offsets computed once plus a scalar offset for the stage's first k
   // (no vector work per load); a ragged last stage checks k per load.
   uint32_t voa[LA], vob[LB];
   OA::template prep<WAVES>(voa, lane, wave, m0, g.M, g.lda);
   OB::template prep<WAVES>(vob, lane, wave, n0, g.N, g.ldb);
-  auto issue_part = [&](int kt, int slot, auto part) {
-    constexpr int P = decltype(part)::value;
-    constexpr int A0 = kSpread ? P * LA / NP : 0, A1 = kSpread ? (P + 1) * LA / NP : LA;
-    constexpr int B0 = kSpread ? P * LB / NP : 0, B1 = kSpread ? (P + 1) * LB / NP : LB;
-    if constexpr (kSpread || P == 0) {
+  // Part `part` of `nparts` of one stage's loads (parts split the per-thread loads evenly).
+  auto issue_part = [&](int kt, int slot, auto part, auto nparts) {
+    constexpr int P = decltype(part)::value, Q = decltype(nparts)::value;
+    constexpr int A0 = P * LA / Q, A1 = (P + 1) * LA / Q;
+    constexpr int B0 = P * LB / Q, B1 = (P + 1) * LB / Q;
+    if constexpr (A1 > A0 || B1 > B0) {
       char* base = smem + slot * kStage;
       const int k0 = kt * BK;
       if (k0 + BK <= g.K) {
@@ -312,8 +337,75 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
 
   // prologue: S-1 stages in flight (stages past the end load zeros: uniform wait counts)
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) static_for<NP>([&](auto pc) { issue_part(kt0 + (s < nk ? s : nk), s, pc); });
+  for (int s = 0; s < S - 1; ++s) issue_part(kt0 + (s < nk ? s : nk), s, ic<0>{}, ic<1>{});
 
+  constexpr int kDs = TM * (A_KM ? 1 : 2) + TN * (B_KM ? 1 : 2);   // LDS reads per k16 step
+  // Interleave the MFMAs of a k16 step with the LDS reads issued before them.
+  auto interleave = [&]() {
+#pragma unroll
+    for (int q = 0; q < TM * TN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (q < kDs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (kDs > TM * TN) __builtin_amdgcn_sched_group_barrier(0x100, kDs - TM * TN, 0);
+  };
+
+  if constexpr (SCHED == 2) {
+    // The stage barrier sits inside the last k16 step: after it, that step's MFMAs (fragments
+    // already in registers) cover the reads of the next stage's first fragments, so the MFMA
+    // pipe does not wait out a barrier plus an LDS round trip at every stage.
+    bf16x8 fa[2][TM], fb[2][TN];
+    // part 0 of stage S-1 goes out with the prologue; each later stage's part 0 is issued right
+    // after the barrier that frees its slot, the other parts over the next NP-1 steps
+    issue_part(kt0 + (S - 1 < nk ? S - 1 : nk), S - 1, ic<0>{}, ic<NP>{});
+    wait_vmcnt<(S - 2) * kLoadsPerThread + LA / NP + LB / NP>();
+    __syncthreads();
+    if (nk > 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(smem, wm * WM + i * 32, 0, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(smem + OA::kBytes, wn * WN + j * 32, 0, lane);
+    }
+    for (int it = 0; it < nk; ++it) {
+      const int nxt = it + S - 1;
+      const int kt_next = kt0 + (nxt < nk ? nxt : nk), slot_next = nxt % S;
+      const char* la = smem + (it % S) * kStage;
+      const char* lb = la + OA::kBytes;
+      const char* la1 = smem + ((it + 1) % S) * kStage;
+      const char* lb1 = la1 + OA::kBytes;
+      static_for<NP>([&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        constexpr int cur = ks & 1;
+        if constexpr (ks + 1 < NP) {
+          issue_part(kt_next, slot_next, ic<ks + 1>{}, ic<NP>{});
+#pragma unroll
+          for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = OA::frag(la, wm * WM + i * 32, ks + 1, lane);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = OB::frag(lb, wn * WN + j * 32, ks + 1, lane);
+        } else {
+          wait_vmcnt<(S - 2) * kLoadsPerThread>();
+          wait_lgkm0();
+          __syncthreads();
+          {
+            const int n2 = it + S;
+            issue_part(kt0 + (n2 < nk ? n2 : nk), n2 % S, ic<0>{}, ic<NP>{});
+          }
+          if (it + 1 < nk) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = OA::frag(la1, wm * WM + i * 32, 0, lane);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = OB::frag(lb1, wn * WN + j * 32, 0, lane);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+        if constexpr (ks + 1 < NP) interleave();
+      });
+    }
+  } else
   for (int it = 0; it < nk; ++it) {
     wait_vmcnt<(S - 2) * kLoadsPerThread>();
     __syncthreads();
@@ -331,7 +423,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
     static_for<NP>([&](auto ksc) {
       constexpr int ks = decltype(ksc)::value;
       constexpr int cur = ks & 1;
-      issue_part(kt_next, slot_next, ksc);
+      issue_part(kt_next, slot_next, ksc, ic<NP>{});
       if constexpr (ks + 1 < NP) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = OA::frag(la, wm * WM + i * 32, ks + 1, lane);
@@ -343,21 +435,13 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
-      if constexpr (SCHED == 1 && ks + 1 < NP) {
-        constexpr int kDs = TM * (A_KM ? 1 : 2) + TN * (B_KM ? 1 : 2);
-#pragma unroll
-        for (int q = 0; q < TM * TN; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (q < kDs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        if constexpr (kDs > TM * TN) __builtin_amdgcn_sched_group_barrier(0x100, kDs - TM * TN, 0);
-      }
+      if constexpr (SCHED == 1 && ks + 1 < NP) interleave();
     });
   }
   wait_vmcnt<0>();
 
   __syncthreads();    // every wave is past its last operand read: the ring becomes epilogue space
-  store_tile<BM, BN, WN, TM, TN, ACC>(g, acc, smem, m0 + wm * WM, n0 + wn * WN, split, lane, wave);
+  store_tile<WM, WN, TM, TN, ACC>(g, acc, smem, m0 + wm * WM, n0 + wn * WN, split, lane, wave);
 }
 
 template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED = 0, int OCC = 1>
@@ -365,7 +449,7 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
   using OA = typename OpSel<A_KM, BM, BK>::T;
   using OB = typename OpSel<B_KM, BN, BK>::T;
   constexpr int ring = S * (OA::kBytes + OB::kBytes);
-  constexpr int epi = WGM * WGN * Epi<BN / WGN, ACC>::kBytes;
+  constexpr int epi = WGM * WGN * EpiOf<BM / WGM, BN / WGN, ACC>::kBytes;
   constexpr int lds = ring > epi ? ring : epi;
   auto kfn = gemm2<BM, BN, BK, S, WGM, WGN, A_KM, B_KM, ACC, SCHED, OCC>;
   static bool attr = false;
@@ -399,6 +483,13 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
 //  12: 256x128, BK 32, 2 stages, 4 waves (128x64 wave tiles), 2 workgroups per CU   LDS 48 KiB
 //  13: 128x256, BK 32, 2 stages, 4 waves (64x128 wave tiles), 2 workgroups per CU   LDS 48 KiB
 //  14: 256x128, BK 32, 3 stages, 4 waves (128x64 wave tiles), 2 workgroups per CU   LDS 72 KiB
+//  15: 256x256, BK 32, 4 stages, 8 waves 2x4, MFMA / LDS-read interleaving          LDS 128 KiB
+//  16: 256x256, BK 32, 5 stages, 8 waves 2x4, MFMA / LDS-read interleaving          LDS 160 KiB
+//  17: 256x256, BK 32, 5 stages, 8 waves 4x2, MFMA / LDS-read interleaving          LDS 160 KiB
+//  18: as 10 with the stage barrier inside the last k16 step
+//  19: as 11 with the stage barrier inside the last k16 step
+//  20: as 12 (256x128, 2 workgroups per CU) with the stage barrier inside the last k16 step
+//  21: as 13 (128x256, 2 workgroups per CU) with the stage barrier inside the last k16 step
 #define SL2_DISPATCH(AK, BKM, ACC)                                                                 \
   switch (g.cfg) {                                                                                 \
     case 0: return sl2::launch_cfg<256, 256, 32, 4, 2, 2, AK, BKM, ACC>(st, g);                   \
@@ -416,6 +507,13 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
     case 12: return sl2::launch_cfg<256, 128, 32, 2, 2, 2, AK, BKM, ACC, 0, 2>(st, g);            \
     case 13: return sl2::launch_cfg<128, 256, 32, 2, 2, 2, AK, BKM, ACC, 0, 2>(st, g);            \
     case 14: return sl2::launch_cfg<256, 128, 32, 3, 2, 2, AK, BKM, ACC, 0, 2>(st, g);            \
+    case 15: return sl2::launch_cfg<256, 256, 32, 4, 2, 4, AK, BKM, ACC, 1>(st, g);               \
+    case 16: return sl2::launch_cfg<256, 256, 32, 5, 2, 4, AK, BKM, ACC, 1>(st, g);               \
+    case 17: return sl2::launch_cfg<256, 256, 32, 5, 4, 2, AK, BKM, ACC, 1>(st, g);               \
+    case 18: return sl2::launch_cfg<256, 256, 64, 2, 2, 4, AK, BKM, ACC, 2>(st, g);               \
+    case 19: return sl2::launch_cfg<256, 256, 64, 2, 4, 2, AK, BKM, ACC, 2>(st, g);               \
+    case 20: return sl2::launch_cfg<256, 128, 32, 2, 2, 2, AK, BKM, ACC, 2, 2>(st, g);            \
+    case 21: return sl2::launch_cfg<128, 256, 32, 2, 2, 2, AK, BKM, ACC, 2, 2>(st, g);            \
     default: return -1;                                                                            \
   }
 
@@ -424,11 +522,11 @@ int gemm2_dgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, false, false) 
 int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) }
 
 void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
-  *bk = (cfg == 0 || cfg == 7 || cfg == 8 || cfg >= 12) ? 32 : 64;
+  *bk = (cfg == 0 || cfg == 7 || cfg == 8 || (cfg >= 12 && cfg <= 17) || cfg >= 20) ? 32 : 64;
   static const int t[kGemm2Configs][2] = {
       {256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256}, {256, 256},
       {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {128, 256},
-      {256, 128}};
+      {256, 128}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {128, 256}};
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }
