@@ -301,8 +301,11 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
 
   const i32x4 ra = rsrc(g.a, g.a_bytes), rb = rsrc(g.b, g.b_bytes);
 
-  // The loads of one stage, split into BK/16 parts issued one per k16 step of the loop.
+  // k16 steps per stage.  The next stage's loads go out over the first kLoadSteps of them: early
+  // enough to land before the stage ends, spread enough not to stall the MFMA stream (measured
+  // best at two steps for BK 64).
   constexpr int NP = BK / 16;
+  constexpr int kLoadSteps = NP < 2 ? NP : 2;
   constexpr int LA = OA::kLoads / WAVES, LB = OB::kLoads / WAVES;
   // Stages wholly inside K use offsets computed once plus a scalar offset for the stage's first k
   // (no vector work per load); a ragged last stage checks k per load.
@@ -414,7 +417,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
     const char* la = smem + (it % S) * kStage;
     const char* lb = la + OA::kBytes;
     // fragments double-buffered in registers: the reads for k16 step ks+1 are in flight while
-    // the MFMAs of step ks issue; the next stage's HBM->LDS loads are spread over the steps
+    // the MFMAs of step ks issue
     bf16x8 fa[2][TM], fb[2][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(la, wm * WM + i * 32, 0, lane);
@@ -423,7 +426,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
     static_for<NP>([&](auto ksc) {
       constexpr int ks = decltype(ksc)::value;
       constexpr int cur = ks & 1;
-      issue_part(kt_next, slot_next, ksc, ic<NP>{});
+      if constexpr (ks < kLoadSteps) issue_part(kt_next, slot_next, ksc, ic<kLoadSteps>{});
       if constexpr (ks + 1 < NP) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = OA::frag(la, wm * WM + i * 32, ks + 1, lane);
