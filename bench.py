@@ -24,6 +24,24 @@ if ROOT not in sys.path:
 METRIC = "TFLOP/s fwd+dgrad+wgrad per TP-sharded linear; % of MI355X MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}      # MI355X published dense MFMA peaks
 HBM_GBS = 8000.0
+# 256 CUs x 2.4 GHz peak engine clock x 4096 bf16 (8192 fp8) dense FLOP per clock per CU
+PEAK_FORMULA = {"bf16": "256 CU x 2.4 GHz x 4096 FLOP/clk/CU = 2.52 PFLOP/s (published 2.5)",
+                "fp8": "256 CU x 2.4 GHz x 8192 FLOP/clk/CU = 5.03 PFLOP/s (published 5.0)"}
+HIP_ATTR_CLOCK_RATE = 5     # hipDeviceAttributeClockRate in hip_runtime_api.h (peak clock, kHz)
+
+
+def device_clock_mhz():
+    """Peak engine clock the HIP runtime reports for device 0 (MHz), or None."""
+    import ctypes
+    from sharded_linear_amd import _lib
+    try:
+        rt = ctypes.CDLL(_lib.hip_runtimes_mapped()[0])
+        v = ctypes.c_int(0)
+        if rt.hipDeviceGetAttribute(ctypes.byref(v), HIP_ATTR_CLOCK_RATE, 0) == 0:
+            return round(v.value / 1000.0, 1)
+    except Exception:
+        pass
+    return None
 
 
 def log(*a):
@@ -33,7 +51,7 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", default="c2")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -174,20 +192,21 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    bounds[0].record(stream)
+    for k in range(args.steps):
         step(timed=not args.no_kernel_events)
-    ev1.record(stream)
+        bounds[k + 1].record(stream)
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = bounds[0].elapsed_time(bounds[-1]) / args.steps
+    step_ms = sorted(bounds[k].elapsed_time(bounds[k + 1]) for k in range(args.steps))
     flops = w.flops_per_step()
     tflops = flops / (ms * 1e-3) / 1e12
     # MXFP8 workload: fwd runs block-scaled fp8 MFMA, dgrad/wgrad bf16 MFMA on the exactly
     # dequantised operand; the bf16 peak is the conservative denominator for the whole step.
     dtype = "mxfp8-e4m3 fwd / bf16 bwd" if w.mxfp8 else "bf16"
     peak = PEAK_TFLOPS["bf16"]
+    med = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
 
     # ---- per-kernel figures from the events -----------------------------------------------
     kinds = {}
@@ -230,9 +249,23 @@ def main():
                    "flops_per_step": flops, "step": "zero grad_data; per micro-batch: fwd of each "
                    "shard, then dgrad + fused fp32 wgrad-accumulate in backward order"},
         "frac_of_peak": round(tflops / peak, 4),
+        "step_ms": {"median": round(med, 4), "min": round(step_ms[0], 4), "max": round(step_ms[-1], 4),
+                    "tflops_at_median": round(flops / (med * 1e-3) / 1e12, 2),
+                    "tflops_at_min": round(flops / (step_ms[0] * 1e-3) / 1e12, 2)},
+        "peak_formula": PEAK_FORMULA["bf16"],
         "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
         "gpu": torch.cuda.get_device_name(dev),
+        "cu_count": torch.cuda.get_device_properties(dev).multi_processor_count,
+        "peak_engine_clock_mhz": device_clock_mhz(),
     }
+    if w.mxfp8:
+        # a third of the FLOPs (fwd) can run at the fp8 rate, two thirds (dgrad, wgrad) at bf16
+        p_mix = 3.0 / (1.0 / PEAK_TFLOPS["fp8"] + 2.0 / PEAK_TFLOPS["bf16"])
+        out["mxfp8_fractions"] = {
+            "of_flop_mix_weighted_peak": round(tflops / p_mix, 4), "flop_mix_weighted_peak": round(p_mix, 1),
+            "of_raw_fp8_peak": round(tflops / PEAK_TFLOPS["fp8"], 4),
+            "per_gemm": {k: round(v["tflops"] / (PEAK_TFLOPS["fp8"] if k == "fwd" else PEAK_TFLOPS["bf16"]), 4)
+                         for k, v in kernels.items() if "tflops" in v}}
     print(json.dumps(out), flush=True)
 
 
@@ -249,6 +282,7 @@ def cpu_baseline(w):
     except Exception:                       # threadpoolctl missing: report the affinity mask
         threads = 0
     cores = threads or len(os.sched_getaffinity(0))
+    host = {"os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "blas_threads": threads}
     if w.mxfp8:
         log("cpu baseline: MXFP8 workload, oracle dequantises per block first")
     names = list(w.step_params)
@@ -272,8 +306,19 @@ def cpu_baseline(w):
         log(f"cpu baseline: micro-batch {k} done, {elapsed:.1f}s")
         if elapsed > 10.0:
             break
+    # the single-core brute-force oracle (pure-Python triple loop) on a slice of config 1
+    c1 = configs.WORKLOADS["c1"]
+    rows = 4
+    Xc = configs.x(c1, "weight", 0)[:rows]
+    Wc = configs.weight(c1, "weight")
+    t = time.perf_counter()
+    ol.fwd_brute(Xc, Wc)
+    tb = time.perf_counter() - t
+    o1, i1 = c1.params["weight"]
+    brute = {"value": round(2 * rows * i1 * o1 / tb / 1e9, 4), "unit": "GFLOP/s", "cores": 1,
+             "sample": f"forward of {rows} of {c1.tokens} rows of config 1 ({o1}x{i1} weight), {tb:.2f}s"}
     return {"value": round(done_flops / elapsed / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "host": host, "brute_force_c1": brute,
             "sample": f"{mbs} of {w.microbatches} micro-batches of the same workload (fwd, dgrad, "
                       f"wgrad-accumulate of every shard), numpy float64, {elapsed:.1f}s"}
 
