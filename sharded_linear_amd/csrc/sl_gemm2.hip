@@ -273,8 +273,7 @@ __device__ __forceinline__ void store_tile(const Gemm2Args& g, f32x16 (&acc)[TM]
 }
 
 // SCHED 0 leaves instruction order to the compiler; SCHED 1 asks it (sched_group_barrier) to
-// alternate MFMAs with the LDS fragment reads of the next k16 step; SCHED 2 does the same and
-// moves the stage barrier into the last k16 step (see the loop).
+// alternate MFMAs with the LDS fragment reads of the next k16 step.
 template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED, int OCC>
 __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
   constexpr int WAVES = WGM * WGN;
@@ -353,62 +352,6 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
     if constexpr (kDs > TM * TN) __builtin_amdgcn_sched_group_barrier(0x100, kDs - TM * TN, 0);
   };
 
-  if constexpr (SCHED == 2) {
-    // The stage barrier sits inside the last k16 step: after it, that step's MFMAs (fragments
-    // already in registers) cover the reads of the next stage's first fragments, so the MFMA
-    // pipe does not wait out a barrier plus an LDS round trip at every stage.
-    bf16x8 fa[2][TM], fb[2][TN];
-    // part 0 of stage S-1 goes out with the prologue; each later stage's part 0 is issued right
-    // after the barrier that frees its slot, the other parts over the next NP-1 steps
-    issue_part(kt0 + (S - 1 < nk ? S - 1 : nk), S - 1, ic<0>{}, ic<NP>{});
-    wait_vmcnt<(S - 2) * kLoadsPerThread + LA / NP + LB / NP>();
-    __syncthreads();
-    if (nk > 0) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) fa[0][i] = OA::frag(smem, wm * WM + i * 32, 0, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[0][j] = OB::frag(smem + OA::kBytes, wn * WN + j * 32, 0, lane);
-    }
-    for (int it = 0; it < nk; ++it) {
-      const int nxt = it + S - 1;
-      const int kt_next = kt0 + (nxt < nk ? nxt : nk), slot_next = nxt % S;
-      const char* la = smem + (it % S) * kStage;
-      const char* lb = la + OA::kBytes;
-      const char* la1 = smem + ((it + 1) % S) * kStage;
-      const char* lb1 = la1 + OA::kBytes;
-      static_for<NP>([&](auto ksc) {
-        constexpr int ks = decltype(ksc)::value;
-        constexpr int cur = ks & 1;
-        if constexpr (ks + 1 < NP) {
-          issue_part(kt_next, slot_next, ic<ks + 1>{}, ic<NP>{});
-#pragma unroll
-          for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = OA::frag(la, wm * WM + i * 32, ks + 1, lane);
-#pragma unroll
-          for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = OB::frag(lb, wn * WN + j * 32, ks + 1, lane);
-        } else {
-          wait_vmcnt<(S - 2) * kLoadsPerThread>();
-          wait_lgkm0();
-          __syncthreads();
-          {
-            const int n2 = it + S;
-            issue_part(kt0 + (n2 < nk ? n2 : nk), n2 % S, ic<0>{}, ic<NP>{});
-          }
-          if (it + 1 < nk) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i) fa[cur ^ 1][i] = OA::frag(la1, wm * WM + i * 32, 0, lane);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) fb[cur ^ 1][j] = OB::frag(lb1, wn * WN + j * 32, 0, lane);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
-        if constexpr (ks + 1 < NP) interleave();
-      });
-    }
-  } else
   for (int it = 0; it < nk; ++it) {
     wait_vmcnt<(S - 2) * kLoadsPerThread>();
     __syncthreads();
@@ -486,13 +429,6 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
 //  12: 256x128, BK 32, 2 stages, 4 waves (128x64 wave tiles), 2 workgroups per CU   LDS 48 KiB
 //  13: 128x256, BK 32, 2 stages, 4 waves (64x128 wave tiles), 2 workgroups per CU   LDS 48 KiB
 //  14: 256x128, BK 32, 3 stages, 4 waves (128x64 wave tiles), 2 workgroups per CU   LDS 72 KiB
-//  15: 256x256, BK 32, 4 stages, 8 waves 2x4, MFMA / LDS-read interleaving          LDS 128 KiB
-//  16: 256x256, BK 32, 5 stages, 8 waves 2x4, MFMA / LDS-read interleaving          LDS 160 KiB
-//  17: 256x256, BK 32, 5 stages, 8 waves 4x2, MFMA / LDS-read interleaving          LDS 160 KiB
-//  18: as 10 with the stage barrier inside the last k16 step
-//  19: as 11 with the stage barrier inside the last k16 step
-//  20: as 12 (256x128, 2 workgroups per CU) with the stage barrier inside the last k16 step
-//  21: as 13 (128x256, 2 workgroups per CU) with the stage barrier inside the last k16 step
 #define SL2_DISPATCH(AK, BKM, ACC)                                                                 \
   switch (g.cfg) {                                                                                 \
     case 0: return sl2::launch_cfg<256, 256, 32, 4, 2, 2, AK, BKM, ACC>(st, g);                   \
@@ -510,13 +446,6 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
     case 12: return sl2::launch_cfg<256, 128, 32, 2, 2, 2, AK, BKM, ACC, 0, 2>(st, g);            \
     case 13: return sl2::launch_cfg<128, 256, 32, 2, 2, 2, AK, BKM, ACC, 0, 2>(st, g);            \
     case 14: return sl2::launch_cfg<256, 128, 32, 3, 2, 2, AK, BKM, ACC, 0, 2>(st, g);            \
-    case 15: return sl2::launch_cfg<256, 256, 32, 4, 2, 4, AK, BKM, ACC, 1>(st, g);               \
-    case 16: return sl2::launch_cfg<256, 256, 32, 5, 2, 4, AK, BKM, ACC, 1>(st, g);               \
-    case 17: return sl2::launch_cfg<256, 256, 32, 5, 4, 2, AK, BKM, ACC, 1>(st, g);               \
-    case 18: return sl2::launch_cfg<256, 256, 64, 2, 2, 4, AK, BKM, ACC, 2>(st, g);               \
-    case 19: return sl2::launch_cfg<256, 256, 64, 2, 4, 2, AK, BKM, ACC, 2>(st, g);               \
-    case 20: return sl2::launch_cfg<256, 128, 32, 2, 2, 2, AK, BKM, ACC, 2, 2>(st, g);            \
-    case 21: return sl2::launch_cfg<128, 256, 32, 2, 2, 2, AK, BKM, ACC, 2, 2>(st, g);            \
     default: return -1;                                                                            \
   }
 
@@ -525,11 +454,11 @@ int gemm2_dgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, false, false) 
 int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) }
 
 void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
-  *bk = (cfg == 0 || cfg == 7 || cfg == 8 || (cfg >= 12 && cfg <= 17) || cfg >= 20) ? 32 : 64;
+  *bk = (cfg == 0 || cfg == 7 || cfg == 8 || cfg >= 12) ? 32 : 64;
   static const int t[kGemm2Configs][2] = {
       {256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256}, {256, 256},
       {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {128, 256},
-      {256, 128}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {128, 256}};
+      {256, 128}};
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }
