@@ -153,6 +153,47 @@ def test_empty_and_degenerate():
     assert torch.equal(G, torch.full((16, 8), 3.0, device="cuda"))
 
 
+@pytest.mark.parametrize("which", ["fwd", "dgrad", "wgrad"])
+def test_operand_beyond_direct_load_extent(which):
+    """One operand of 2 GiB or more: too large for the direct HBM->LDS loads' 32-bit offsets, so
+    the GEMM runs on the register-staged kernel.  The big operand repeats a seeded block of P rows
+    (plus a ragged tail of R rows), which lets the oracle check fwd / dgrad on sampled rows and
+    the weight gradient exactly as reps x (block product) + tail product."""
+    P, reps, R = 4096, 64, 520
+    T = P * reps + R                       # 262,664 rows
+    big, small = 4096, 64                  # 262,664 x 4096 bf16 = 2.15 GB
+    say(f"case big operand {which}: T={T} big={big} small={small}")
+    blk_big = synth.normal_bf16((P, big), 7001)
+    blk_small = synth.normal_bf16((P, small), 7002)
+
+    def tiled(blk):
+        d = dev_bf16(blk)
+        return torch.cat([d.repeat(reps, 1), d[:R]], dim=0)
+
+    rows = np.r_[0:40, P * 17 + 5:P * 17 + 45, T - 40:T]
+    if which == "fwd":                     # X [T, big] huge, W [small, big]
+        W = synth.normal_bf16((small, big), 7003, synth.W_STD)
+        X = tiled(blk_big)
+        Y = sl.sl_linear_fwd(X, dev_bf16(W))
+        torch.cuda.synchronize()
+        ref = ol.linear_fwd(blk_big[rows % P], W)
+        assert ol.rel_err(host_f64(Y[torch.as_tensor(rows, device="cuda")]), ref) <= TOL_BF16
+    elif which == "dgrad":                 # dY [T, big] huge, W [big, small]
+        W = synth.normal_bf16((big, small), 7004, synth.W_STD)
+        dY = tiled(blk_big)
+        dX = sl.sl_linear_dgrad(dY, dev_bf16(W))
+        torch.cuda.synchronize()
+        ref = ol.linear_dgrad(blk_big[rows % P], W)
+        assert ol.rel_err(host_f64(dX[torch.as_tensor(rows, device="cuda")]), ref) <= TOL_BF16
+    else:                                  # X [T, big] huge, dY [T, small]: main_grad [small, big]
+        X, dY = tiled(blk_big), tiled(blk_small)
+        G = torch.zeros((small, big), device="cuda")
+        sl.sl_linear_wgrad_accum(X, dY, G)
+        torch.cuda.synchronize()
+        ref = reps * ol.linear_wgrad(blk_big, blk_small) + ol.linear_wgrad(blk_big[:R], blk_small[:R])
+        assert ol.rel_err(host_f64(G), ref) <= TOL_F32
+
+
 def test_neighbours_and_padding_untouched():
     """A wgrad into one view of grad_data leaves every other element bit-identical."""
     say("case neighbours and padding")
