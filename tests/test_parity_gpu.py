@@ -326,6 +326,33 @@ def test_mxfp8_all_codes_decode_exactly(n_in):
         assert np.array_equal(Y, want), s
 
 
+def test_mxfp8_dequantised_operand_exact():
+    """The dequantised MXFP8 operand of dgrad and wgrad, bit for bit: with dY = I (T = out), dgrad
+    returns deq(Wq) and the weight gradient returns deq(Xq), each element one exact product.
+    Every finite E4M3 code appears under each of four block scales."""
+    say("case mxfp8 dequantised operand, all codes")
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)   # 254 codes
+    n = 256                                   # out = T = 256 rows, in = 4 blocks of 64 codes
+    q = np.zeros((n, 256), np.uint8)
+    q.reshape(-1)[: codes.size * 4] = np.tile(codes, 4)
+    sc = np.empty((n, 8), np.uint8)
+    sc[:] = np.array([100, 120, 127, 135, 127, 135, 100, 120], np.uint8)
+    eye = np.zeros((n, n), np.float32)
+    np.fill_diagonal(eye, 1.0)
+    I = dev_bf16(synth.f32_to_bf16_bits(eye))
+    ws = torch.zeros(sl.sl_mxfp8_workspace_bytes(n, 256, n), dtype=torch.uint8, device="cuda")
+    # dgrad: dX[T=n, in] = I . deq(Wq[out=n, in])
+    dX = sl.sl_linear_dgrad_mxfp8w(I, dev_u8(q), dev_u8(sc), workspace=ws)
+    # weight gradient: main_grad[out=n, in] += I^T . deq(Xq[T=n, in])
+    G = torch.zeros((n, 256), device="cuda")
+    sl.sl_linear_wgrad_accum_mxfp8x(dev_u8(q), dev_u8(sc), I, G, workspace=ws)
+    torch.cuda.synchronize()
+    from oracle import numerics
+    want = numerics.mxfp8_dequant(q, sc)
+    assert np.array_equal(host_f64(dX), want)
+    assert np.array_equal(host_f64(G), want)
+
+
 # ---------------------------------------------------------------------------------------------
 # Full-size workloads (launch configuration of the benchmark), sampled against the oracle
 # ---------------------------------------------------------------------------------------------
