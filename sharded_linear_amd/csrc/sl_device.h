@@ -51,9 +51,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // One 16-byte-per-lane HBM->LDS load: lane i writes LDS [lds + 16 i, +16).  Issued as inline
 // assembly so that the compiler does not guard every later LDS read with a full vmcnt wait;
-// the kernel orders these loads itself with wait_vmcnt<>() and a barrier.
+// the kernel orders these loads itself with wait_vmcnt<>() and a barrier.  gfx9 parts need one
+// wait state between a scalar write of M0 and an LDS DMA that reads it; the compiler cannot see
+// the DMA inside the assembly, so the s_nop provides it.
 __device__ __forceinline__ void lds_dma16(i32x4 rs, uint32_t lds, uint32_t voff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rs), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rs), "{m0}"(lds) : "memory");
 }
 
 // As lds_dma16, with a wave-uniform byte offset `soff` added to the address.  Lanes whose voff
@@ -61,12 +63,12 @@ __device__ __forceinline__ void lds_dma16(i32x4 rs, uint32_t lds, uint32_t voff)
 // with soff added (the caller only uses it that way), so the result does not depend on whether
 // the range check includes soff.
 __device__ __forceinline__ void lds_dma16s(i32x4 rs, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds) : "memory");
 }
 
 // One 4-byte-per-lane HBM->LDS load: lane i writes LDS [lds + 4 i, +4).
 __device__ __forceinline__ void lds_dma4(i32x4 rs, uint32_t lds, uint32_t voff) {
-  asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(rs), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(rs), "{m0}"(lds) : "memory");
 }
 
 // E4M3FN code times 2^(s - 127) as bf16 bits.  Value = sig * 2^(max(e,1) - 10) with

@@ -417,12 +417,11 @@ int pick_config(int64_t M, int64_t N) {
   return best;
 }
 
-Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a_bytes, int64_t b_bytes) {
+Plan make_plan_cfg(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a_bytes, int64_t b_bytes,
+                   int cfg) {
   Plan p{};
   p.v2 = !mxfp8 && a_bytes <= kMaxDmaBytes && b_bytes <= kMaxDmaBytes;
   if (p.v2) {
-    int cfg = config_override(kind);
-    if (cfg < 0) cfg = kind == Kind::Wgrad ? 10 : pick_config(M, N);
     p.cfg = cfg;
     gemm2_tile(cfg, &p.bm, &p.bn, &p.bk);
   } else {
@@ -444,6 +443,28 @@ Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a
   if (per < 1) per = 1;
   p.kps = int(per);
   p.splits = int(nkt == 0 ? 1 : (nkt + per - 1) / per);
+  return p;
+}
+
+Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a_bytes, int64_t b_bytes) {
+  int cfg = config_override(kind);
+  if (cfg < 0) {
+    cfg = kind == Kind::Wgrad ? 10 : pick_config(M, N);
+    // 256x256 tiles: the fixed-order kernels measured ahead of the compiler-scheduled one.  The
+    // weight gradient (both operands MN-major, whole cache lines per 32-k row) takes 4 waves with
+    // a 4-stage ring of 32 k; forward products take 8 waves with 2 stages of 64 k (a 32-k row of
+    // a K-major operand is half a cache line); dgrad, with one operand of each kind, the first
+    // for long K and the second otherwise.
+    if (cfg == 10) cfg = kind == Kind::Wgrad ? 15 : kind == Kind::Fwd ? 17 : (K >= 6144 ? 15 : 17);
+  }
+  Plan p = make_plan_cfg(kind, mxfp8, M, N, K, a_bytes, b_bytes, cfg);
+  // configurations that prefill a deep ring need that many k stages in every split
+  if (p.v2) {
+    const int64_t nkt = (K + p.bk - 1) / p.bk;
+    const int64_t last = nkt - int64_t(p.splits - 1) * p.kps;
+    const int need = gemm2_min_stages(p.cfg);
+    if (p.kps < need || last < need) p = make_plan_cfg(kind, mxfp8, M, N, K, a_bytes, b_bytes, 10);
+  }
   return p;
 }
 

@@ -17,7 +17,7 @@ struct Gemm2Args {
   int cfg;              // tile configuration, see gemm2_tile()
 };
 
-constexpr int kGemm2Configs = 15;
+constexpr int kGemm2Configs = 19;
 
 // A K-major (k contiguous) and B K-major: forward.
 int gemm2_fwd(hipStream_t st, Gemm2Args g);
@@ -27,3 +27,5 @@ int gemm2_dgrad(hipStream_t st, Gemm2Args g);
 int gemm2_wgrad(hipStream_t st, Gemm2Args g);
 // Macro-tile (and k extent of one LDS stage) of configuration cfg.
 void gemm2_tile(int cfg, int* bm, int* bn, int* bk);
+// Fewest k stages each split must have under configuration cfg.
+int gemm2_min_stages(int cfg);

@@ -35,12 +35,13 @@ struct KMaj {
   static constexpr int kBytes = R * kRowBytes;
   static constexpr int kLoads = kBytes / 1024;         // wave-loads of 1 KiB per stage
   static_assert(BK == 32 || BK == 64, "row swizzles are defined for BK 32 and 64");
-  // XOR swizzle of 16-byte chunks: 8 consecutive rows (a 128-byte bank window per 8 lanes of a
-  // 32-bank LDS phase) and 16 consecutive rows (256 bytes per 16 lanes of a 64-bank phase)
-  // reading the same logical chunk all land on distinct banks.
+  // XOR swizzle of 16-byte chunks by row, chosen by measurement: a wave's ds_read_b128 of one
+  // fragment (32 rows, two chunks) runs at the rate of linear addresses -- full LDS rate with 8
+  // waves per CU -- with these, while the 64-byte-row alternative ((r >> 1) ^ (r >> 3)) & 3,
+  // conflict-free on paper for 8 and 16 consecutive lanes, ran 1.7x slower.
   __device__ static __forceinline__ int swz(int r) {
     if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);
-    else return ((r >> 1) ^ (r >> 3)) & 3;
+    else return (r ^ (r >> 2)) & 3;
   }
 
   // Wave `w` issues loads wl = w, w + waves, ...; lane i fills LDS bytes [1024 wl + 16 i, +16).
@@ -390,6 +391,257 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
   store_tile<WM, WN, TM, TN, ACC>(g, acc, smem, m0 + wm * WM, n0 + wn * WN, split, lane, wave);
 }
 
+// ---- 4-wave kernel with a fixed issue order ------------------------------------------------------
+// One wave per SIMD, each computing a 128x128 quarter of a 256x256 tile (16 accumulators), so a
+// k16 step is 16 MFMAs against 8 fragment reads.  The LDS ring holds S stages of 32 k; the loads
+// of stage s + S go out right after the barrier that ends the reads of stage s, so every load has
+// S - 1 stages of MFMA work to land.  Each k16 step interleaves its 16 MFMAs with the fragment
+// reads of the next step and, in a stage's second step, the HBM->LDS loads; sched_barrier fences
+// keep exactly that order.  The stage barrier sits between a stage's two steps: the second
+// step's fragments are already in registers, so its MFMAs cover the first reads of the next stage
+// issued just after the barrier, and no wave starts a stage waiting on LDS.
+//
+// Barrier B(s+1), between the steps of stage s, certifies (i) every wave's loads of stage s + 1
+// have landed (each wave waits for its own with vmcnt first) and (ii) every wave has read all of
+// stage s (its second-step fragments were waited for), so its slot can take stage s + S.
+template <bool A_KM, bool B_KM, bool ACC, int S, int WGM, int WGN, int BK_>
+struct G4 {
+  static constexpr int BM = 256, BN = 256, BK = BK_, WAVES = WGM * WGN, WM = BM / WGM, WN = BN / WGN;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  using OA = typename OpSel<A_KM, BM, BK>::T;
+  using OB = typename OpSel<B_KM, BN, BK>::T;
+  static constexpr int kStage = OA::kBytes + OB::kBytes;
+  static constexpr int LA = OA::kLoads / WAVES, LB = OB::kLoads / WAVES, LPS = LA + LB;
+  static constexpr int kRing = S * kStage;
+  static constexpr int kEpi = WAVES * EpiOf<WM, WN, ACC>::kBytes;
+  static constexpr int kLds = kRing > kEpi ? kRing : kEpi;
+  static_assert(OA::kLoads % WAVES == 0 && OB::kLoads % WAVES == 0, "loads per wave");
+  static_assert(S >= 2 && kLds <= 160 * 1024, "ring");
+};
+
+// Per-lane LDS byte offset of the first fragment (32 rows from r0) of a K-major operand for k16
+// step ks, relative to the operand's base in a stage.  The row swizzle repeats every 32 rows, so
+// the other fragments add immediates; steps change the swizzled chunk and need their own offset.
+template <class O>
+__device__ __forceinline__ uint32_t kmaj_frag_off(int r0, int ks, int lane) {
+  const int r = r0 + (lane & 31), c = ks * 2 + (lane >> 5);
+  return uint32_t(r * O::kRowBytes + ((c ^ O::swz(r)) << 4));
+}
+// Same for an MN-major operand's first transposing read (k rows kb..kb+3 of step 0).  The chunk
+// swizzle of these rows depends on k % 4 only, so steps (16 rows) and the second read (4 rows
+// further) are immediates; fragments differ in their swizzled chunk and need their own offsets.
+template <class O>
+__device__ __forceinline__ uint32_t mnmaj_frag_off(int f0, int lane) {
+  const int g = lane >> 4, s = lane & 15, j = s >> 2, q = s & 3;
+  const int f = f0 + 16 * (g & 1) + 4 * q;
+  const int k = 8 * (g >> 1) + j;
+  return uint32_t(k * O::kRowBytes + (((f >> 3) ^ O::swz(k)) << 4) + ((f & 7) << 1));
+}
+
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_rd128(uint32_t addr) {
+  const auto* p = reinterpret_cast<const __attribute__((address_space(3))) uint4*>(addr + OFF);
+  return __builtin_bit_cast(bf16x8, *p);
+}
+template <int OFF0, int OFF1>
+__device__ __forceinline__ bf16x8 lds_rd_tr(uint32_t addr) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr + OFF0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr + OFF1));
+  const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int N>
+__device__ __forceinline__ void asm_wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" : : "i"(N) : "memory"); }
+
+template <bool A_KM, bool B_KM, bool ACC, int S, int WGM, int WGN, int BK_>
+__global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
+  using P = G4<A_KM, B_KM, ACC, S, WGM, WGN, BK_>;
+  using OA = typename P::OA;
+  using OB = typename P::OB;
+  constexpr int BK = P::BK, WAVES = P::WAVES, WM = P::WM, WN = P::WN, TM = P::TM, TN = P::TN;
+  constexpr int LA = P::LA, LB = P::LB, LPS = P::LPS, kStage = P::kStage;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  int m0, n0;
+  tile_origin<P::BM, P::BN>(g, m0, n0);
+  const int split = blockIdx.z;
+  const int nkt = (g.K + BK - 1) / BK;
+  const int kt0 = split * g.kt_per_split;
+  const int nk = min(nkt, kt0 + g.kt_per_split) - kt0;
+
+  const i32x4 ra = rsrc(g.a, g.a_bytes), rb = rsrc(g.b, g.b_bytes);
+  // load offsets relative to a stage's first k; the ragged last stage (K % 32 != 0) uses a copy
+  // with the lanes past K sent out of range
+  uint32_t voa[LA], vob[LB], vra[LA], vrb[LB];
+  OA::template prep<WAVES>(voa, lane, wave, m0, g.M, g.lda);
+  OB::template prep<WAVES>(vob, lane, wave, n0, g.N, g.ldb);
+  {
+    const int kr = g.K - (nkt - 1) * BK;          // k extent of the last stage
+#pragma unroll
+    for (int it = 0; it < LA; ++it) {
+      const int p = (it * WAVES + wave) * 64 + lane;
+      const int kk = A_KM ? ((p % OA::kCPR) ^ OA::swz(p / OA::kCPR)) * 8 : p / OA::kCPR;
+      vra[it] = kk < kr ? voa[it] : kOOB;
+    }
+#pragma unroll
+    for (int it = 0; it < LB; ++it) {
+      const int p = (it * WAVES + wave) * 64 + lane;
+      const int kk = B_KM ? ((p % OB::kCPR) ^ OB::swz(p / OB::kCPR)) * 8 : p / OB::kCPR;
+      vrb[it] = kk < kr ? vob[it] : kOOB;
+    }
+  }
+  const uint32_t ka_step = A_KM ? BK * 2 : uint32_t(BK * g.lda * 2);
+  const uint32_t kb_step = B_KM ? BK * 2 : uint32_t(BK * g.ldb * 2);
+  const uint32_t lds0 = lds_addr(smem);
+
+  // fragment read offsets (per lane), K-major: one per k16 step; MN-major: one per fragment
+  constexpr int NPS = BK / 16;
+  uint32_t ofa[A_KM ? NPS : TM], ofb[B_KM ? NPS : TN];
+  if constexpr (A_KM)
+#pragma unroll
+    for (int ks = 0; ks < NPS; ++ks) ofa[ks] = kmaj_frag_off<OA>(wm * WM, ks, lane);
+  else
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ofa[i] = mnmaj_frag_off<OA>(wm * WM + 32 * i, lane);
+  if constexpr (B_KM)
+#pragma unroll
+    for (int ks = 0; ks < NPS; ++ks) ofb[ks] = OA::kBytes + kmaj_frag_off<OB>(wn * WN, ks, lane);
+  else
+#pragma unroll
+    for (int j = 0; j < TN; ++j) ofb[j] = OA::kBytes + mnmaj_frag_off<OB>(wn * WN + 32 * j, lane);
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  bf16x8 fa[2][TM], fb[2][TN];
+
+  // fragment i (A) or j (B) of k16 step ks from the stage at LDS byte `base`
+  auto read_a = [&](bf16x8& d, uint32_t base, auto ic_i, auto ic_ks) {
+    constexpr int i = decltype(ic_i)::value, ks = decltype(ic_ks)::value;
+    if constexpr (A_KM) d = lds_rd128<i * 32 * OA::kRowBytes>(base + ofa[ks]);
+    else d = lds_rd_tr<ks * 16 * OA::kRowBytes, (ks * 16 + 4) * OA::kRowBytes>(base + ofa[i]);
+  };
+  auto read_b = [&](bf16x8& d, uint32_t base, auto ic_j, auto ic_ks) {
+    constexpr int j = decltype(ic_j)::value, ks = decltype(ic_ks)::value;
+    if constexpr (B_KM) d = lds_rd128<j * 32 * OB::kRowBytes>(base + ofb[ks]);
+    else d = lds_rd_tr<ks * 16 * OB::kRowBytes, (ks * 16 + 4) * OB::kRowBytes>(base + ofb[j]);
+  };
+  // wave-load `l` (A: l < LA, then B) of the stage at k tile kt into LDS slot `slot`
+  auto load_one = [&](auto ic_l, int kt, int slot, bool ragged) {
+    constexpr int l = decltype(ic_l)::value;
+    const uint32_t base = lds0 + slot * kStage;
+    if constexpr (l < LA) {
+      lds_dma16s(ra, base + (l * WAVES + wave) * 1024, ragged ? vra[l] : voa[l], uint32_t(kt) * ka_step);
+    } else {
+      constexpr int lb = l - LA;
+      lds_dma16s(rb, base + OA::kBytes + (lb * WAVES + wave) * 1024, ragged ? vrb[lb] : vob[lb], uint32_t(kt) * kb_step);
+    }
+  };
+  // Memory operation m of a step: m < NR reads fragment piece m into buffer NX; after that the
+  // loads [L0, L0 + LPS/2) of stage kt into slot `slot` (when `loads`).
+  constexpr int NR = TM + TN, LH = LPS / 2;
+  static_assert(LPS % 2 == 0, "loads split over two steps");
+  auto memop = [&](auto ic_m, auto ic_nx, auto ic_ks, auto ic_l0, uint32_t rbase, bool loads, int kt, int slot,
+                   bool ragged) {
+    constexpr int m = decltype(ic_m)::value, nx = decltype(ic_nx)::value, l0 = decltype(ic_l0)::value;
+    if constexpr (m < NR) {
+      if constexpr (m < TM) read_a(fa[nx][m], rbase, ic<m>{}, ic_ks);
+      else read_b(fb[nx][m - TM], rbase, ic<m - TM>{}, ic_ks);
+    } else {
+      if (loads) load_one(ic<l0 + m - NR>{}, kt, slot, ragged);
+    }
+  };
+  // One k16 step: TM x TN MFMAs on buffer CUR; NM memory operations spread over them.
+  auto step = [&](auto ic_cur, auto ic_nm, auto&& mem) {
+    constexpr int cur = decltype(ic_cur)::value, NM = decltype(ic_nm)::value;
+    static_for<TM * TN>([&](auto qc) {
+      constexpr int q = decltype(qc)::value, i = q / TN, j = q % TN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+      constexpr int lo = q * NM / (TM * TN), hi = (q + 1) * NM / (TM * TN);
+      static_for<hi - lo>([&](auto mc) { mem(ic<lo + decltype(mc)::value>{}); });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  {
+    // Prologue: stages 0..S-2 and the first half of stage S-1 (the host launches this kernel only
+    // when every split has at least S stages).  From then on the loads of stage x are issued in two
+    // halves: the first in the second step of stage x - S (just after the barrier that frees its
+    // slot), the second in the first step of stage x - S + 1, which spreads them over the MFMAs.
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const bool rag = kt0 + s == nkt - 1;
+      if (s < S - 1) static_for<LPS>([&](auto lc) { load_one(lc, kt0 + s, s, rag); });
+      else static_for<LH>([&](auto lc) { load_one(lc, kt0 + s, s, rag); });
+    }
+    // stage 0 is complete once at most the S-2 later stages' loads (the last one only half issued)
+    // are outstanding
+    asm_wait_vm<LPS * (S - 2) + LH>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<TM>([&](auto ic_i) { read_a(fa[0][decltype(ic_i)::value], lds0, ic_i, ic<0>{}); });
+    static_for<TN>([&](auto ic_j) { read_b(fb[0][decltype(ic_j)::value], lds0, ic_j, ic<0>{}); });
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Stage s: steps 0 .. NPS-2, each on buffer t % 2 and reading step t + 1 into the other (the
+    // first also issues the second half of stage s + S - 1); barrier; the last step on buffer 1
+    // (NPS is even), reading the next stage's step 0 into buffer 0 and issuing the first half of
+    // stage s + S into s's slot.  At the barrier the loads issued after the last one of stage
+    // s + 1 are the S - 2 whole stages s + 2 .. s + S - 1.
+    constexpr int NPS_ = BK / 16;
+    static_assert(NPS_ % 2 == 0, "steps per stage");
+    auto stage = [&](int s, auto ic_vm, auto ic_la, auto ic_lb, auto ic_last) {
+      constexpr int VM = decltype(ic_vm)::value;
+      constexpr bool LDA = decltype(ic_la)::value, LDB = decltype(ic_lb)::value, LAST = decltype(ic_last)::value;
+      const int slot = s % S;
+      const uint32_t cur = lds0 + slot * kStage;
+      static_for<NPS_ - 1>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr bool ld = LDA && t == 0;
+        const int kt = kt0 + s + S - 1, lslot = (s + S - 1) % S;
+        const bool rag = kt == nkt - 1;
+        step(ic<t % 2>{}, ic<ld ? NR + LH : NR>{},
+             [&](auto ic_m) { memop(ic_m, ic<(t + 1) % 2>{}, ic<t + 1>{}, ic<LH>{}, cur, ld, kt, lslot, rag); });
+      });
+      if constexpr (!LAST) {
+        asm_wait_vm<VM>();
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t nxt = lds0 + ((s + 1) % S) * kStage;
+        const int kt = kt0 + s + S;
+        const bool rag = kt == nkt - 1;
+        step(ic<1>{}, ic<LDB ? NR + LH : NR>{},
+             [&](auto ic_m) { memop(ic_m, ic<0>{}, ic<0>{}, ic<0>{}, nxt, LDB, kt, slot, rag); });
+      } else {
+        step(ic<1>{}, ic<0>{}, [&](auto) {});
+      }
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    for (int s = 0; s < nk - S; ++s) stage(s, ic<LPS * (S - 2)>{}, T_{}, T_{}, F_{});
+    // The last S stages issue no new stages (the first still completes stage nk - 1); stage
+    // nk-S+j waits for stage nk-S+j+1, after which S-2-j whole stages remain outstanding.
+    static_for<S>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j == S - 1) stage(nk - S + j, ic<0>{}, std::bool_constant<j == 0>{}, F_{}, T_{});
+      else stage(nk - S + j, ic<(S - 2 - j) * LPS>{}, std::bool_constant<j == 0>{}, F_{}, F_{});
+    });
+  }
+  asm_wait_vm<0>();
+  __syncthreads();    // every wave is past its last operand read: the ring becomes epilogue space
+  store_tile<WM, WN, TM, TN, ACC>(g, acc, smem, m0 + wm * WM, n0 + wn * WN, split, lane, wave);
+}
+
 template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED = 0, int OCC = 1>
 int launch_cfg(hipStream_t st, Gemm2Args g) {
   using OA = typename OpSel<A_KM, BM, BK>::T;
@@ -407,6 +659,27 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
   g.tiles_m = (g.M + BM - 1) / BM;
   g.tiles_n = (g.N + BN - 1) / BN;
   hipLaunchKernelGGL(kfn, dim3(g.tiles_m * g.tiles_n, 1, g.splits), dim3(WGM * WGN * 64), lds, st, g);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+template <int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int BK = 32>
+int launch_g4(hipStream_t st, Gemm2Args g) {
+  using P = G4<A_KM, B_KM, ACC, S, WGM, WGN, BK>;
+  auto kfn = gemm4<A_KM, B_KM, ACC, S, WGM, WGN, BK>;
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, P::kLds) != hipSuccess)
+      return -5;
+    attr = true;
+  }
+  // every split needs at least S stages of 32 k: the prologue fills the whole ring (the planner
+  // gives shorter products to another configuration)
+  const int nkt = (g.K + P::BK - 1) / P::BK;
+  const int last = nkt - (g.splits - 1) * g.kt_per_split;
+  if (g.kt_per_split < S || last < S) return -1;
+  g.tiles_m = (g.M + P::BM - 1) / P::BM;
+  g.tiles_n = (g.N + P::BN - 1) / P::BN;
+  hipLaunchKernelGGL(kfn, dim3(g.tiles_m * g.tiles_n, 1, g.splits), dim3(P::WAVES * 64), P::kLds, st, g);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
@@ -429,6 +702,10 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
 //  12: 256x128, BK 32, 2 stages, 4 waves (128x64 wave tiles), 2 workgroups per CU   LDS 48 KiB
 //  13: 128x256, BK 32, 2 stages, 4 waves (64x128 wave tiles), 2 workgroups per CU   LDS 48 KiB
 //  14: 256x128, BK 32, 3 stages, 4 waves (128x64 wave tiles), 2 workgroups per CU   LDS 72 KiB
+//  15: 256x256, BK 32, 4 stages, 4 waves (128x128 wave tiles), fixed issue order        LDS 128 KiB
+//  16: 256x256, BK 32, 4 stages, 8 waves 2x4 (128x64 wave tiles), fixed issue order     LDS 128 KiB
+//  17: 256x256, BK 64, 2 stages, 8 waves 2x4 (128x64 wave tiles), fixed issue order     LDS 128 KiB
+//  18: 256x256, BK 64, 2 stages, 4 waves (128x128 wave tiles), fixed issue order        LDS 128 KiB
 #define SL2_DISPATCH(AK, BKM, ACC)                                                                 \
   switch (g.cfg) {                                                                                 \
     case 0: return sl2::launch_cfg<256, 256, 32, 4, 2, 2, AK, BKM, ACC>(st, g);                   \
@@ -446,6 +723,10 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
     case 12: return sl2::launch_cfg<256, 128, 32, 2, 2, 2, AK, BKM, ACC, 0, 2>(st, g);            \
     case 13: return sl2::launch_cfg<128, 256, 32, 2, 2, 2, AK, BKM, ACC, 0, 2>(st, g);            \
     case 14: return sl2::launch_cfg<256, 128, 32, 3, 2, 2, AK, BKM, ACC, 0, 2>(st, g);            \
+    case 15: return sl2::launch_g4<4, 2, 2, AK, BKM, ACC>(st, g);                                  \
+    case 16: return sl2::launch_g4<4, 2, 4, AK, BKM, ACC>(st, g);                                  \
+    case 17: return sl2::launch_g4<2, 2, 4, AK, BKM, ACC, 64>(st, g);                              \
+    case 18: return sl2::launch_g4<2, 2, 2, AK, BKM, ACC, 64>(st, g);                              \
     default: return -1;                                                                            \
   }
 
@@ -453,12 +734,14 @@ int gemm2_fwd(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, true, false) }
 int gemm2_dgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, false, false) }
 int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) }
 
+int gemm2_min_stages(int cfg) { return cfg == 15 || cfg == 16 ? 4 : cfg == 17 || cfg == 18 ? 2 : 1; }
+
 void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
-  *bk = (cfg == 0 || cfg == 7 || cfg == 8 || cfg >= 12) ? 32 : 64;
+  *bk = (cfg == 0 || cfg == 7 || cfg == 8 || (cfg >= 12 && cfg <= 16)) ? 32 : 64;
   static const int t[kGemm2Configs][2] = {
       {256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256}, {256, 256},
       {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {128, 256},
-      {256, 128}};
+      {256, 128}, {256, 256}, {256, 256}, {256, 256}, {256, 256}};
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }
