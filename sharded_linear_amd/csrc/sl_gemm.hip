@@ -625,6 +625,15 @@ namespace {
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Block-scaled fp8 forward configuration: 256x256 tiles (8 waves) when they fill the chip, else
+// 128x128.  SL_F8_CONFIG="<n>" forces configuration n (0 or 1).
+int f8_config(int64_t T, int64_t out) {
+  const char* e = getenv("SL_F8_CONFIG");
+  const int cfg = (e && *e) ? atoi(e) : -1;
+  if (cfg == 0 || cfg == 1) return cfg;
+  return ntiles(T, out, 256, 256) >= 200 ? 0 : 1;
+}
+
 bool f8_native(int64_t T, int64_t in, int64_t out, const void* Xs, const void* Ws) {
   return in % 128 == 0 && aligned4(Xs) && aligned4(Ws) && T * in <= kMaxDmaBytes && out * in <= kMaxDmaBytes;
 }
@@ -672,7 +681,7 @@ extern "C" int sl_linear_fwd_mxfp8(void* stream, const uint8_t* Xq, const uint8_
     g.a_bytes = uint32_t(T * in); g.b_bytes = uint32_t(out * in);
     g.sa_bytes = uint32_t(T * (in / 32)); g.sb_bytes = uint32_t(out * (in / 32));
     g.M = int(T); g.N = int(out); g.K = int(in);
-    g.cfg = ntiles(T, out, 256, 256) >= 200 ? 0 : 1;
+    g.cfg = f8_config(T, out);
     return f8_fwd(hs, g) == 0 ? SL_OK : SL_EHIP;
   }
   const Plan p = make_plan(Kind::Fwd, true, T, out, in, T * in, out * in);

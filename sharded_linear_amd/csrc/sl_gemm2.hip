@@ -133,18 +133,6 @@ struct MNMaj {
   }
 };
 
-template <int I>
-using ic = std::integral_constant<int, I>;
-
-// Calls f(ic<0>), ..., f(ic<N-1>): a compile-time loop.
-template <int N, int I = 0, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(ic<I>{});
-    static_for<N, I + 1>(f);
-  }
-}
-
 template <bool KM, int R, int BK>
 struct OpSel { using T = KMaj<R, BK>; };
 template <int R, int BK>

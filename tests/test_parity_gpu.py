@@ -307,6 +307,21 @@ def test_mxfp8_elementwise(T, n_in, n_out):
     assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
 
 
+@pytest.mark.parametrize("cfg", range(2))
+@pytest.mark.parametrize("T,n_in,n_out", [(300, 384, 520), (1000, 512, 776), (2050, 1024, 264), (4100, 256, 3336)])
+def test_mxfp8_fwd_every_config(monkeypatch, cfg, T, n_in, n_out):
+    """Each block-scaled fp8 forward configuration, forced through SL_F8_CONFIG, on ragged M/N."""
+    say(f"case mxfp8 fwd cfg={cfg} T={T} in={n_in} out={n_out}")
+    monkeypatch.setenv("SL_F8_CONFIG", str(cfg))
+    Xq, Xs = synth.mxfp8_normal((T, n_in), 31 + cfg)
+    Wq, Ws = synth.mxfp8_normal((n_out, n_in), 32 + cfg, synth.W_STD)
+    Y = sl.sl_linear_fwd_mxfp8(dev_u8(Xq), dev_u8(Xs), dev_u8(Wq), dev_u8(Ws))
+    torch.cuda.synchronize()
+    e_y = ol.rel_err(host_f64(Y), ol.linear_fwd_mxfp8(Xq, Xs, Wq, Ws))
+    say(f"  rel err Y {e_y:.2e}")
+    assert e_y <= TOL_BF16
+
+
 @pytest.mark.parametrize("n_in", [32, 128])
 def test_mxfp8_all_codes_decode_exactly(n_in):
     """Every finite E4M3 code under several scales: a one-hot fwd returns the decoded value
