@@ -148,3 +148,19 @@ def rel_err(got, ref) -> float:
     if den == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return float(num / den)
+
+
+# ---- MXFP8 backward as well ([GTP] section 1.3: forward and backward GEMMs in MXFP8, each GEMM
+# reading copies quantised along its own contraction axis; the weight gradient is accumulated in
+# fp32 as above) --------------------------------------------------------------------------------
+
+def linear_dgrad_mxfp8(dYq, dYs, WqT, WsT):
+    """dX = deq(dY rowwise) . deq(W columnwise): dY quantised along ``out`` ([T, out] codes), W
+    quantised along ``out`` and stored transposed ([in, out] codes)."""
+    return mxfp8_dequant(dYq, dYs) @ mxfp8_dequant(WqT, WsT).T
+
+
+def linear_wgrad_accum_mxfp8(main_grad, dYqT, dYsT, XqT, XsT):
+    """main_grad + deq(dY columnwise) . deq(X columnwise)^T: both quantised along T and stored
+    transposed ([out, T] and [in, T] codes)."""
+    return np.asarray(main_grad, dtype=np.float64) + mxfp8_dequant(dYqT, dYsT) @ mxfp8_dequant(XqT, XsT).T

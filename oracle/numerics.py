@@ -9,6 +9,12 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 * E8M0 (the MX shared scale): an unsigned biased exponent, value 2^(e-127); 0xFF is NaN.
 * MX block size 32 along the contraction axis ([GTP] section 1.3, "Communication volume
   breakdown": one scale byte per 32 elements, 1/32 B per element).
+* MX quantisation (the pages fix only the block of 32 and per-block scaling with no tensor-wide
+  amax, [GTP] section 1.3; the rule below is the OCP Microscaling v1.0 conversion): per block,
+  shared exponent X = floor(log2 amax) - 8 (8 = the largest E4M3 exponent) clamped to
+  [-127, 127] and stored biased by 127; each element x / 2^X rounded to the nearest E4M3 value,
+  ties to the even code, saturating at +-448; the sign of x is kept (a negative element that
+  rounds to zero is -0); an all-zero block stores scale 0 and zero codes.
 """
 from __future__ import annotations
 
@@ -58,3 +64,43 @@ def mxfp8_dequant(codes: np.ndarray, scales: np.ndarray, block: int = 32) -> np.
     assert k % block == 0 and scales.shape[-1] == k // block
     v = e4m3_to_f64(codes).reshape(*codes.shape[:-1], k // block, block)
     return (v * e8m0_to_f64(scales)[..., None]).reshape(codes.shape)
+
+
+def _e4m3_encode_nonneg(r: np.ndarray) -> np.ndarray:
+    """Code of non-negative E4M3 values (exact grid points), through the inverse table."""
+    lut = {float(E4M3_TABLE[c]): c for c in range(0x7F)}
+    return np.vectorize(lambda v: lut[float(v)], otypes=[np.uint8])(r)
+
+
+def mx_quantize(x: np.ndarray, block: int = 32):
+    """MX-quantise real ``x`` along its last axis into (E4M3 codes, E8M0 scales), in float64.
+
+    Follows the OCP MX v1.0 conversion stated in the module docstring, step by step:
+    floor(log2 amax) comes from frexp (amax = m 2^E, m in [0.5, 1) -> E - 1), the division by
+    2^X is exact in float64, and rounding to the E4M3 grid uses the grid spacing of the value's
+    binade (2^(e-3) for normals, 2^-9 below 2^-6) with numpy's round-half-even.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    k = x.shape[-1]
+    assert k % block == 0 and np.all(np.isfinite(x))
+    xb = x.reshape(-1, k // block, block)
+    amax = np.abs(xb).max(axis=-1)
+    zero = amax == 0
+    _, E = np.frexp(np.where(zero, 1.0, amax))
+    X = np.clip(E - 1 - 8, -127, 127)
+    v = xb / np.exp2(X)[..., None]
+    a = np.abs(v)
+    _, ea = np.frexp(np.where(a == 0, 1.0, a))
+    q = np.where(a >= 2.0 ** -6, np.exp2(ea - 1 - 3), 2.0 ** -9)       # grid spacing at a
+    r = np.minimum(np.rint(a / q) * q, 448.0)
+    codes = _e4m3_encode_nonneg(r) | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
+    codes[np.broadcast_to(zero[..., None], codes.shape)] = 0
+    scales = np.where(zero, 0, X + 127).astype(np.uint8)
+    return codes.reshape(x.shape).astype(np.uint8), scales.reshape(*x.shape[:-1], k // block)
+
+
+def mx_quantize_cols(x: np.ndarray, block: int = 32):
+    """Columnwise MX quantisation of a 2-D ``x`` [R, C]: blocks of 32 run down the columns and the
+    result is stored transposed, codes [C, R] and scales [C, R/32] -- the layout in which a GEMM
+    contracting over R reads it with k contiguous."""
+    return mx_quantize(np.asarray(x, dtype=np.float64).T, block)

@@ -381,3 +381,95 @@ def test_quantiser_matches_scalar_rule():
     for b in range(x.shape[0]):
         codes, sc = _scalar_e4m3_quant(x[b])
         assert s[b, 0] == sc and list(q[b]) == codes, b
+
+
+# ---- the oracle's own MX quantiser (the quantisation step of the MXFP8 backward path) ----------
+
+def test_oracle_quantiser_matches_scalar_rule():
+    """numerics.mx_quantize against the element-by-element nearest-grid search above, on normal
+    draws of several magnitudes, exact ties, saturating values, zeros and signed zeros."""
+    rng = np.random.default_rng(18)
+    blocks = [rng.standard_normal(32) * s for s in (1, 0.02, 3e-3, 7e4, 1e-30)]
+    tie = np.array([1.0, 1.0625, 1.1875, 0.25 + 2 ** -11, 2 ** -14, 2 ** -16 * 3] + [0.5] * 26)
+    signed_zero = np.array([-0.0, 0.0, 3.0] + [-2.0 ** -12] * 29)
+    blocks += [tie, -tie, np.full(32, 460.0), np.zeros(32), signed_zero]
+    x = np.stack(blocks)
+    q, s = numerics.mx_quantize(x)
+    for b in range(x.shape[0]):
+        codes, sc = _scalar_e4m3_quant(x[b])
+        assert s[b, 0] == sc and list(q[b]) == codes, b
+
+
+def test_oracle_quantiser_every_bf16_below_the_block_max():
+    """Every positive finite bf16 magnitude up to 256, each in a block whose maximum is 256
+    (shared exponent 0): the code is the nearest E4M3 value, ties to even, by brute force."""
+    bits = np.arange(1, 0x4380 + 1, dtype=np.uint32)                   # bf16 0x0001 .. 256.0
+    vals = (bits << 16).view(np.float32).astype(np.float64)
+    vals = vals[vals <= 256.0]
+    n = (vals.size + 30) // 31
+    x = np.full((n, 32), 0.0)
+    x[:, 31] = 256.0
+    x[:, :31].flat[: vals.size] = vals
+    q, s = numerics.mx_quantize(x)
+    assert np.all(s == 127)
+    grid = np.array(sorted({numerics.e4m3_value(c) for c in range(0x7F)}))
+    codes = np.array(sorted(range(0x7F), key=numerics.e4m3_value))
+    got = q[:, :31].flat[: vals.size]
+    lo = np.searchsorted(grid, vals, side="right") - 1
+    hi = np.minimum(lo + 1, grid.size - 1)
+    dlo, dhi = vals - grid[lo], grid[hi] - vals
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(codes[lo] % 2 == 0, lo, hi)))
+    assert np.array_equal(got, codes[pick])
+
+
+def test_oracle_quantiser_scale_range_and_bound():
+    """amax / 2^X lies in [256, 512) for unclamped blocks; |x - deq| is at most half a grid step
+    (2^(e-4) for an element of binade 2^e after scaling) below the saturation point."""
+    rng = np.random.default_rng(19)
+    x = rng.standard_normal((64, 128)) * np.exp2(rng.integers(-20, 20, (64, 1)))
+    q, s = numerics.mx_quantize(x)
+    X = s.astype(np.int64) - 127
+    amax = np.abs(x.reshape(64, 4, 32)).max(-1)
+    ratio = amax / np.exp2(X)
+    assert np.all((ratio >= 256) & (ratio < 512))
+    back = numerics.mxfp8_dequant(q, s)
+    v = np.abs(x.reshape(64, 4, 32)) / np.exp2(X)[..., None]
+    step = np.where(v >= 2.0 ** -6, np.exp2(np.floor(np.log2(np.maximum(v, 2.0 ** -6))) - 3), 2.0 ** -9)
+    err = np.abs(x - back).reshape(64, 4, 32) / np.exp2(X)[..., None]
+    ok = (v > 448) | (err <= step / 2 + 1e-300)
+    assert np.all(ok)
+
+
+def test_columnwise_quantisation_blocks_run_down_columns():
+    """A column whose 32-row blocks are power-of-two multiples of E4M3 values round-trips exactly
+    through the transposed columnwise copy.  (Codes with mantissa 7 are left out: a block maximum
+    of 1.875 * 2^e scales to 480 and saturates to 448 under the shared-exponent rule.)"""
+    rng = np.random.default_rng(20)
+    codes = rng.integers(0, 0x7F, (64, 96)).astype(np.uint8)
+    codes[(codes & 7) == 7] -= 1
+    x = numerics.e4m3_to_f64(codes) * np.exp2(rng.integers(-10, 10, (1, 96)))
+    q, s = numerics.mx_quantize_cols(x)
+    assert q.shape == (96, 64) and s.shape == (96, 2)
+    back = numerics.mxfp8_dequant(q, s)
+    assert np.array_equal(back, x.T)
+
+
+@pytest.mark.parametrize("T,n_in,n_out", [(32, 32, 32), (64, 96, 32), (96, 32, 64)])
+def test_mxfp8_backward_products_brute_force(T, n_in, n_out):
+    """dgrad and wgrad over both-MXFP8 operands equal the triple loops over the dequantised
+    values, with the weight and the gradients in the layouts the kernels read."""
+    rng = np.random.default_rng(T + n_in + n_out)
+    dY = rng.standard_normal((T, n_out))
+    W = rng.standard_normal((n_out, n_in)) * 0.02
+    X = rng.standard_normal((T, n_in))
+    G0 = rng.standard_normal((n_out, n_in))
+    dYq, dYs = numerics.mx_quantize(dY)
+    WqT, WsT = numerics.mx_quantize_cols(W)
+    dYqT, dYsT = numerics.mx_quantize_cols(dY)
+    XqT, XsT = numerics.mx_quantize_cols(X)
+    dX = linear.linear_dgrad_mxfp8(dYq, dYs, WqT, WsT)
+    want = linear.dgrad_brute(numerics.mxfp8_dequant(dYq, dYs), numerics.mxfp8_dequant(WqT, WsT).T)
+    assert np.allclose(dX, want, rtol=1e-12, atol=1e-12)
+    G = linear.linear_wgrad_accum_mxfp8(G0, dYqT, dYsT, XqT, XsT)
+    want = linear.wgrad_accum_brute(G0, numerics.mxfp8_dequant(XqT, XsT).T, numerics.mxfp8_dequant(dYqT, dYsT).T)
+    assert np.allclose(G, want, rtol=1e-12, atol=1e-12)
