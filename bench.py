@@ -134,6 +134,17 @@ def main():
         else:
             buf.param(n).copy_(dev_bf16(wt))
     xs, dys = [], []
+    qb = {}
+    if w.mxfp8_all:
+        # MXFP8 copies made inside the step: W, X and dY rowwise ([r, c] codes, [r, c/32] scales) and
+        # columnwise (transposed: [c, r] codes, [c, r/32] scales)
+        def quant_bufs(r, c):
+            u8 = dict(dtype=torch.uint8, device=dev)
+            return (torch.empty((r, c), **u8), torch.empty((r, c // 32), **u8),
+                    torch.empty((c, r), **u8), torch.empty((c, r // 32), **u8))
+        for n in names:
+            o, i = w.params[n]
+            qb[n] = {"W": quant_bufs(o, i), "X": quant_bufs(w.tokens, i), "dY": quant_bufs(w.tokens, o)}
     for k in range(w.microbatches):
         xk, dyk = {}, {}
         for n in names:
@@ -148,7 +159,8 @@ def main():
     wss = {}
     for n in names:
         o, i = w.params[n]
-        nb = sl.sl_mxfp8_workspace_bytes(T, i, o) if w.mxfp8 else sl.sl_wgrad_workspace_bytes(T, i, o)
+        nb = (sl.sl_mxfp8_workspace_bytes(T, i, o) if w.mxfp8 else
+              sl.sl_mxfp8_wgrad_workspace_bytes(T, i, o) if w.mxfp8_all else sl.sl_wgrad_workspace_bytes(T, i, o))
         wss[n] = torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev) if nb else None
     torch.cuda.synchronize()
     log(f"set-up {time.time() - t0:.1f}s: {w.title}; grad_data {buf.numel} elements")
@@ -170,6 +182,8 @@ def main():
 
     def step(timed=False):
         launch("zero", 0, sl.sl_grad_buffer_zero, buf.grad_data, timed=timed)
+        if w.mxfp8_all:
+            return step_mxfp8_all(timed)
         for k in range(w.microbatches):
             for n in names:
                 o, i = w.params[n]
@@ -189,6 +203,27 @@ def main():
                     launch("dgrad", f, sl.sl_linear_dgrad, dys[k][n], buf.param(n), dxs[n], timed=timed)
                     launch("wgrad", f, sl.sl_linear_wgrad_accum, xs[k][n], dys[k][n], buf.main_grad(n),
                            wss[n], timed=timed)
+
+    def step_mxfp8_all(timed):
+        # weights: quantised once per step (fixed across its micro-batches), both directions
+        for n in names:
+            launch("quant", 0, sl.sl_mxfp8_quantize, buf.param(n), True, True, qb[n]["W"], timed=timed)
+        for k in range(w.microbatches):
+            for n in names:
+                o, i = w.params[n]
+                Xq, Xs, _, _ = qb[n]["X"]
+                Wq, Ws, _, _ = qb[n]["W"]
+                launch("quant", 0, sl.sl_mxfp8_quantize, xs[k][n], True, True, qb[n]["X"], timed=timed)
+                launch("fwd", 2 * T * i * o, sl.sl_linear_fwd_mxfp8, Xq, Xs, Wq, Ws, ys[n], timed=timed)
+            for n in reversed(names):
+                o, i = w.params[n]
+                dYq, dYs, dYqT, dYsT = qb[n]["dY"]
+                _, _, WqT, WsT = qb[n]["W"]
+                _, _, XqT, XsT = qb[n]["X"]
+                launch("quant", 0, sl.sl_mxfp8_quantize, dys[k][n], True, True, qb[n]["dY"], timed=timed)
+                launch("dgrad", 2 * T * i * o, sl.sl_linear_dgrad_mxfp8, dYq, dYs, WqT, WsT, dxs[n], timed=timed)
+                launch("wgrad", 2 * T * i * o, sl.sl_linear_wgrad_accum_mxfp8, dYqT, dYsT, XqT, XsT,
+                       buf.main_grad(n), wss[n], timed=timed)
 
     for _ in range(args.warmup):
         step()
@@ -213,8 +248,8 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     # MXFP8 workload: fwd runs block-scaled fp8 MFMA, dgrad/wgrad bf16 MFMA on the exactly
     # dequantised operand; the bf16 peak is the conservative denominator for the whole step.
-    dtype = "mxfp8-e4m3 fwd / bf16 bwd" if w.mxfp8 else "bf16"
-    peak = PEAK_TFLOPS["bf16"]
+    dtype = "mxfp8-e4m3 fwd / bf16 bwd" if w.mxfp8 else "mxfp8-e4m3" if w.mxfp8_all else "bf16"
+    peak = PEAK_TFLOPS["fp8"] if w.mxfp8_all else PEAK_TFLOPS["bf16"]
     med = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
 
     # ---- per-kernel figures from the events -----------------------------------------------
@@ -237,7 +272,7 @@ def main():
         dom = max(gemm, key=lambda k: gemm[k]["ms"])
         d = gemm[dom]
         ach = d["flops"] / (d["ms"] * 1e-3) / 1e12
-        kpeak = PEAK_TFLOPS["fp8"] if (w.mxfp8 and dom == "fwd") else peak
+        kpeak = PEAK_TFLOPS["fp8"] if ((w.mxfp8 and dom == "fwd") or w.mxfp8_all) else peak
         roofline = {"kernel": f"linear_{dom}", "bound": "mfma", "achieved": round(ach, 1), "peak": kpeak,
                     "unit": "TFLOP/s", "frac": round(ach / kpeak, 4),
                     "traffic": stored_traffic(w.key, f"linear_{dom}"),
@@ -256,12 +291,14 @@ def main():
         "config": {"workload": w.title, "key": w.key, "tokens": T, "microbatches": w.microbatches,
                    "shards_out_in": {n: list(w.params[n]) for n in names},
                    "flops_per_step": flops, "step": "zero grad_data; per micro-batch: fwd of each "
-                   "shard, then dgrad + fused fp32 wgrad-accumulate in backward order"},
+                   "shard, then dgrad + fused fp32 wgrad-accumulate in backward order" +
+                   ("; W quantised once per step, X before fwd and dY before dgrad, each rowwise and "
+                    "columnwise (MXFP8 quantisation kernels inside the timed step)" if w.mxfp8_all else "")},
         "frac_of_peak": round(tflops / peak, 4),
         "step_ms": {"median": round(med, 4), "min": round(step_ms[0], 4), "max": round(step_ms[-1], 4),
                     "tflops_at_median": round(flops / (med * 1e-3) / 1e12, 2),
                     "tflops_at_min": round(flops / (step_ms[0] * 1e-3) / 1e12, 2)},
-        "peak_formula": PEAK_FORMULA["bf16"],
+        "peak_formula": PEAK_FORMULA["fp8" if w.mxfp8_all else "bf16"],
         "roofline": roofline, "kernels": kernels, "cpu_baseline": cpu,
         "gpu": torch.cuda.get_device_name(dev),
         "cu_count": torch.cuda.get_device_properties(dev).multi_processor_count,
@@ -297,6 +334,8 @@ def cpu_baseline(w):
     names = list(w.step_params)
     weights = {n: configs.weight(w, n) for n in names}
     done_flops, elapsed, mbs = 0, 0.0, 0
+    if w.mxfp8_all:
+        return cpu_baseline_mxfp8_all(w, names, weights, cores, host)
     for k in range(w.microbatches):
         xk = {n: configs.x(w, n, k) for n in names}
         dyk = {n: configs.dy(w, n, k) for n in names}
@@ -329,6 +368,47 @@ def cpu_baseline(w):
     return {"value": round(done_flops / elapsed / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle", "host": host, "brute_force_c1": brute,
             "sample": f"{mbs} of {w.microbatches} micro-batches of the same workload (fwd, dgrad, "
+                      f"wgrad-accumulate of every shard), numpy float64, {elapsed:.1f}s"}
+
+
+def cpu_baseline_mxfp8_all(w, names, weights, cores, host):
+    """The oracle on the all-MXFP8 workload: quantisation of W (once) and of X and dY (per
+    micro-batch, rowwise and columnwise) in float64, then the products over the dequantised
+    values, on the first 1024 tokens of each micro-batch until about 10 s have passed."""
+    import numpy as np
+    from oracle import linear as ol
+    from oracle import numerics
+    from synth import configs
+
+    rows = 1024
+    t = time.perf_counter()
+    wq = {}
+    for n in names:
+        wf = numerics.bf16_bits_to_f64(weights[n])
+        wq[n] = (numerics.mx_quantize(wf), numerics.mx_quantize_cols(wf))
+    elapsed, done_flops, mbs = time.perf_counter() - t, 0, 0
+    for k in range(w.microbatches):
+        xk = {n: configs.x(w, n, k)[:rows] for n in names}
+        dyk = {n: configs.dy(w, n, k)[:rows] for n in names}
+        t = time.perf_counter()
+        for n in names:
+            (wr, ws_), (wcq, wcs) = wq[n]
+            xf, dyf = numerics.bf16_bits_to_f64(xk[n]), numerics.bf16_bits_to_f64(dyk[n])
+            xr, xc, dr, dc = (numerics.mx_quantize(xf), numerics.mx_quantize_cols(xf),
+                              numerics.mx_quantize(dyf), numerics.mx_quantize_cols(dyf))
+            ol.linear_fwd_mxfp8(*xr, wr, ws_)
+            ol.linear_dgrad_mxfp8(*dr, wcq, wcs)
+            ol.linear_wgrad_accum_mxfp8(np.zeros(w.params[n]), *dc, *xc)
+        elapsed += time.perf_counter() - t
+        done_flops += sum(6 * rows * o * i for o, i in (w.params[n] for n in names))
+        mbs += 1
+        log(f"cpu baseline: micro-batch {k} slice done, {elapsed:.1f}s")
+        if elapsed > 10.0:
+            break
+    return {"value": round(done_flops / elapsed / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "host": host,
+            "sample": f"first {rows} of {w.tokens} tokens of {mbs} of {w.microbatches} micro-batches (weight "
+                      f"quantisation once, X/dY quantisation rowwise and columnwise, fwd, dgrad, "
                       f"wgrad-accumulate of every shard), numpy float64, {elapsed:.1f}s"}
 
 

@@ -140,6 +140,46 @@ int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, const uint8_t*
                                  const void* dY, float* main_grad, int64_t T, int64_t in,
                                  int64_t out, void* workspace, size_t workspace_bytes);
 
+/* ---------------------------------------------------------------------------------------------
+ * All-MXFP8 step: the backward GEMMs in MXFP8 as well (NVIDIA Megatron-Core guide "Generalized
+ * Tensor Parallelism", section 1.3: in the MXFP8 recipe each GEMM reads E4M3 elements with one
+ * E8M0 scale per 32 elements along its own contraction axis; the weight gradient still
+ * accumulates into fp32 main_grad, section 3.1).  A tensor read along both axes is quantised
+ * twice: rowwise (blocks along the last axis) and columnwise (blocks down the columns, stored
+ * transposed so that the consuming GEMM reads k contiguously).
+ *   fwd:   sl_linear_fwd_mxfp8 with X, W rowwise                      (above)
+ *   dgrad: dX[T,in]         = deq(dYq)[T,out] . deq(WqT)[in,out]^T    dY rowwise, W columnwise
+ *   wgrad: main_grad[out,in] += deq(dYqT)[out,T] . deq(XqT)[in,T]^T   dY and X columnwise
+ *
+ * sl_mxfp8_quantize: x[rows, cols] bf16 (row-major, 16-byte aligned) into rowwise codes
+ * q_rows[rows, cols] + scales s_rows[rows, cols/32] and/or columnwise codes q_cols[cols, rows] +
+ * scales s_cols[cols, rows/32]; a NULL pair is skipped (each code pointer must come with its
+ * scale pointer: SL_EINVAL otherwise).  The rowwise copy needs cols % 32 == 0, the columnwise
+ * copy rows % 32 == 0 and cols % 8 == 0 (SL_ESHAPE).  The rule is the OCP MX v1.0 conversion (the pages fix only
+ * the block and per-block scaling): per block X = clamp(floor(log2 amax) - 8, -127, 127),
+ * scale byte X + 127, codes = E4M3 round-to-nearest-even of x / 2^X saturating at +-448 with
+ * the sign kept; an all-zero block stores scale 0 and zero codes.  Inputs must be finite
+ * (non-finite elements give unspecified codes).  Code pointers 16-byte aligned.
+ *
+ * sl_linear_dgrad_mxfp8 / sl_linear_wgrad_accum_mxfp8: the contraction extent (out for dgrad,
+ * T for wgrad) must be a multiple of 128, in/out multiples of 8 (SL_ESHAPE); code pointers
+ * 16-byte aligned, scale pointers 4-byte aligned (SL_EALIGN).  The weight gradient takes a
+ * device workspace of at least sl_mxfp8_wgrad_workspace_bytes(T, in, out) bytes (fp32 split-K
+ * planes [splits][out][in]; 0 when the shape needs no split, workspace may then be NULL); its
+ * initial contents do not matter, a split call launches a second, reducing kernel on the same
+ * stream, and concurrent calls need distinct workspaces.  main_grad is read and written only
+ * inside its [out, in] extent.
+ * ------------------------------------------------------------------------------------------- */
+int sl_mxfp8_quantize(void* stream, const void* x, int64_t rows, int64_t cols, uint8_t* q_rows,
+                      uint8_t* s_rows, uint8_t* q_cols, uint8_t* s_cols);
+int sl_linear_dgrad_mxfp8(void* stream, const uint8_t* dYq, const uint8_t* dYs, const uint8_t* WqT,
+                          const uint8_t* WsT, void* dX, int64_t T, int64_t in, int64_t out);
+size_t sl_mxfp8_wgrad_workspace_bytes(int64_t T, int64_t in, int64_t out);
+int sl_linear_wgrad_accum_mxfp8(void* stream, const uint8_t* dYqT, const uint8_t* dYsT,
+                                const uint8_t* XqT, const uint8_t* XsT, float* main_grad,
+                                int64_t T, int64_t in, int64_t out, void* workspace,
+                                size_t workspace_bytes);
+
 #ifdef __cplusplus
 }
 #endif

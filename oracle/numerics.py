@@ -66,10 +66,15 @@ def mxfp8_dequant(codes: np.ndarray, scales: np.ndarray, block: int = 32) -> np.
     return (v * e8m0_to_f64(scales)[..., None]).reshape(codes.shape)
 
 
+_NONNEG_CODES = np.arange(0x7F, dtype=np.uint8)          # 0x00 .. 0x7E: 0 .. 448, increasing
+
+
 def _e4m3_encode_nonneg(r: np.ndarray) -> np.ndarray:
-    """Code of non-negative E4M3 values (exact grid points), through the inverse table."""
-    lut = {float(E4M3_TABLE[c]): c for c in range(0x7F)}
-    return np.vectorize(lambda v: lut[float(v)], otypes=[np.uint8])(r)
+    """Code of non-negative E4M3 values (exact grid points), through the inverse of the table."""
+    grid = E4M3_TABLE[:0x7F]
+    idx = np.searchsorted(grid, r)
+    assert np.all(grid[idx] == r), "not an E4M3 grid point"
+    return _NONNEG_CODES[idx]
 
 
 def mx_quantize(x: np.ndarray, block: int = 32):

@@ -35,6 +35,11 @@ PROTOTYPES = {
     "sl_linear_dgrad_mxfp8w": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_sz]),
     "sl_linear_wgrad_accum_mxfp8x": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
                                                     c_vp, c_sz]),
+    "sl_mxfp8_quantize": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
+    "sl_linear_dgrad_mxfp8": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64]),
+    "sl_mxfp8_wgrad_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64]),
+    "sl_linear_wgrad_accum_mxfp8": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
+                                                   c_vp, c_sz]),
 }
 
 _lib = None

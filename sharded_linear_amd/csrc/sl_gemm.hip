@@ -745,3 +745,97 @@ extern "C" int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, con
   st = run_v1<false, false, Elem::BF16, Elem::MXFP8, Epi::AccumF32>(hs, a, p);
   return st ? st : reduce_splits(hs, a);
 }
+
+// ---- all-MXFP8 step: quantisation and the both-MXFP8 dgrad / wgrad --------------------------
+
+namespace {
+
+// Split-K of the fp8 weight gradient (256x256 tiles, 128-k stages): fill ~256 CUs with output
+// tiles, keep at least 8 stages per split, at most 16 splits.
+F8Args f8_wgrad_plan(int64_t T, int64_t in, int64_t out) {
+  F8Args g{};
+  g.M = int(out); g.N = int(in); g.K = int(T);
+  g.cfg = 0;
+  const int64_t tiles = ntiles(out, in, 256, 256), nkt = T / 128;
+  int64_t s = tiles < 200 ? (256 + tiles / 2) / tiles : 1;
+  if (s > nkt / 8) s = nkt / 8;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  const int64_t per = (nkt + s - 1) / s;
+  g.kt_per_split = int(per);
+  g.splits = int((nkt + per - 1) / per);
+  return g;
+}
+
+bool f8_extents_ok(int64_t a_bytes, int64_t b_bytes) { return a_bytes <= kMaxDmaBytes && b_bytes <= kMaxDmaBytes; }
+
+}  // namespace
+
+extern "C" int sl_mxfp8_quantize(void* stream, const void* x, int64_t rows, int64_t cols, uint8_t* q_rows,
+                                 uint8_t* s_rows, uint8_t* q_cols, uint8_t* s_cols) {
+  if (rows < 0 || cols < 0) return SL_EINVAL;
+  if (rows >= kMaxExtent || cols >= kMaxExtent) return SL_ESHAPE;
+  if (!q_rows != !s_rows || !q_cols != !s_cols) return SL_EINVAL;
+  if ((q_rows && cols % 32) || (q_cols && (rows % 32 || cols % 8))) return SL_ESHAPE;
+  if (rows == 0 || cols == 0 || (!q_rows && !q_cols)) return SL_OK;
+  if (!x) return SL_EINVAL;
+  if (!aligned16(x) || (q_rows && !aligned16(q_rows)) || (q_cols && !aligned16(q_cols))) return SL_EALIGN;
+  return mx_quantize(static_cast<hipStream_t>(stream), x, rows, cols, q_rows, s_rows, q_cols, s_cols) == 0 ? SL_OK
+                                                                                                        : SL_EHIP;
+}
+
+extern "C" int sl_linear_dgrad_mxfp8(void* stream, const uint8_t* dYq, const uint8_t* dYs, const uint8_t* WqT,
+                                     const uint8_t* WsT, void* dX, int64_t T, int64_t in, int64_t out) {
+  int st = check_dims(T, in, out, 8);
+  if (st) return st;
+  if (out % 128) return SL_ESHAPE;
+  if (T == 0 || in == 0) return SL_OK;
+  if (!dX || (out > 0 && (!dYq || !dYs || !WqT || !WsT))) return SL_EINVAL;
+  if (!aligned16(dX) || (out > 0 && (!aligned16(dYq) || !aligned16(WqT) || !aligned4(dYs) || !aligned4(WsT))))
+    return SL_EALIGN;
+  if (!f8_extents_ok(T * out, in * out)) return SL_ESHAPE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  F8Args g{};   // out == 0: the kernel runs no k stage and stores zeros
+  g.a = dYq; g.b = WqT; g.sa = dYs; g.sb = WsT; g.c = dX;
+  g.lda = out; g.ldb = out; g.ldc = in;
+  g.a_bytes = uint32_t(T * out); g.b_bytes = uint32_t(in * out);
+  g.sa_bytes = uint32_t(T * (out / 32)); g.sb_bytes = uint32_t(in * (out / 32));
+  g.M = int(T); g.N = int(in); g.K = int(out);
+  g.cfg = f8_config(T, in);
+  return f8_fwd(hs, g) == 0 ? SL_OK : SL_EHIP;
+}
+
+extern "C" size_t sl_mxfp8_wgrad_workspace_bytes(int64_t T, int64_t in, int64_t out) {
+  if (T <= 0 || in <= 0 || out <= 0 || T % 128) return 0;
+  const F8Args g = f8_wgrad_plan(T, in, out);
+  return g.splits > 1 ? size_t(int64_t(g.splits) * out * in * 4) : 0;
+}
+
+extern "C" int sl_linear_wgrad_accum_mxfp8(void* stream, const uint8_t* dYqT, const uint8_t* dYsT, const uint8_t* XqT,
+                                           const uint8_t* XsT, float* main_grad, int64_t T, int64_t in, int64_t out,
+                                           void* workspace, size_t workspace_bytes) {
+  int st = check_dims(T, in, out, 8);
+  if (st) return st;
+  if (T % 128) return SL_ESHAPE;
+  if (T == 0 || in == 0 || out == 0) return SL_OK;
+  if (!dYqT || !dYsT || !XqT || !XsT || !main_grad) return SL_EINVAL;
+  if (!aligned16(dYqT) || !aligned16(XqT) || !aligned16(main_grad) || !aligned4(dYsT) || !aligned4(XsT))
+    return SL_EALIGN;
+  if (!f8_extents_ok(out * T, in * T)) return SL_ESHAPE;
+  F8Args g = f8_wgrad_plan(T, in, out);
+  if (g.splits > 1) {
+    if (!workspace || !aligned16(workspace) || workspace_bytes < sl_mxfp8_wgrad_workspace_bytes(T, in, out))
+      return SL_EWORKSPACE;
+    g.ws = static_cast<float*>(workspace);
+  }
+  g.a = dYqT; g.b = XqT; g.sa = dYsT; g.sb = XsT; g.c = main_grad;
+  g.lda = T; g.ldb = T; g.ldc = in;
+  g.a_bytes = uint32_t(out * T); g.b_bytes = uint32_t(in * T);
+  g.sa_bytes = uint32_t(out * (T / 32)); g.sb_bytes = uint32_t(in * (T / 32));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (f8_accum(hs, g)) return SL_EHIP;
+  if (g.splits <= 1) return SL_OK;
+  Args a{};
+  a.M = g.M; a.N = g.N; a.c = main_grad; a.ldc = in; a.splits = g.splits; a.ws = g.ws;
+  return reduce_splits(hs, a);
+}

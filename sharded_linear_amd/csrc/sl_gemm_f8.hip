@@ -84,7 +84,7 @@ struct F8Tile {
   }
 };
 
-template <int BM, int BN, int S, int WGM, int WGN>
+template <int BM, int BN, int S, int WGM, int WGN, bool ACC>
 __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
   constexpr int WAVES = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
@@ -111,7 +111,10 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
   const int tm = first_m + (t % (8 * g.tiles_n)) % gsz;
   const int tn = (t % (8 * g.tiles_n)) / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int nk = (g.K + kF8RowBytes - 1) / kF8RowBytes;
+  const int split = blockIdx.z;
+  const int nkt = (g.K + kF8RowBytes - 1) / kF8RowBytes;
+  const int kt0 = ACC ? split * g.kt_per_split : 0;
+  const int nk = ACC ? min(nkt, kt0 + g.kt_per_split) - kt0 : nkt;
 
   const i32x4 ra = rsrc(g.a, g.a_bytes), rb = rsrc(g.b, g.b_bytes);
   const i32x4 rsa = rsrc(g.sa, g.sa_bytes), rsb = rsrc(g.sb, g.sb_bytes);
@@ -134,14 +137,14 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(s < nk ? s : nk, s);
+  for (int s = 0; s < S - 1; ++s) issue(kt0 + (s < nk ? s : nk), s);
 
   for (int it = 0; it < nk; ++it) {
     wait_vmcnt<(S - 2) * kLoadsPerWave>();
     __syncthreads();
     {
       const int nxt = it + S - 1;
-      issue(nxt < nk ? nxt : nk, nxt % S);
+      issue(kt0 + (nxt < nk ? nxt : nk), nxt % S);
     }
     const char* la = smem + (it % S) * kStage;
     const char* lb = la + TA::kBytes;
@@ -171,6 +174,32 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
   wait_vmcnt<0>();
 
   const int rib = 4 * (lane >> 5), cib = lane & 31;
+  if constexpr (ACC) {
+    // fp32 result: lanes 0..31 of each row cover 32 consecutive columns (128 bytes).  Unsplit:
+    // the single read-modify-write of C; split: this split's partial into its own plane.
+    const bool direct = g.splits == 1;
+    float* C = direct ? static_cast<float*>(g.c) : g.ws + int64_t(split) * g.M * g.N;
+    const int64_t ldc = direct ? g.ldc : g.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WN + j * 32 + cib;
+        const int mb = m0 + wm * WM + i * 32 + rib;
+        float old[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = mb + 8 * (r >> 2) + (r & 3);
+          old[r] = (direct && m < g.M && n < g.N) ? C[int64_t(m) * ldc + n] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = mb + 8 * (r >> 2) + (r & 3);
+          if (m < g.M && n < g.N) C[int64_t(m) * ldc + n] = old[r] + acc[i][j][r];
+        }
+      }
+    return;
+  }
   const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
   __bf16* C = static_cast<__bf16*>(g.c);
 #pragma unroll
@@ -239,11 +268,11 @@ __global__ void mx_dequant_bf16(const uint8_t* codes, const uint8_t* scales, uin
   }
 }
 
-template <int BM, int BN, int S, int WGM, int WGN>
+template <int BM, int BN, int S, int WGM, int WGN, bool ACC = false>
 int launch_f8(hipStream_t st, F8Args g) {
   constexpr int lds = S * (F8Tile<BM>::kBytes + F8Tile<BN>::kBytes +
                            ((F8Tile<BM>::kScaleBytes + F8Tile<BN>::kScaleBytes + 255) / 256) * 256 + 256);
-  auto kfn = gemm_f8fwd<BM, BN, S, WGM, WGN>;
+  auto kfn = gemm_f8fwd<BM, BN, S, WGM, WGN, ACC>;
   static bool attr = false;
   if (!attr) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
@@ -252,7 +281,7 @@ int launch_f8(hipStream_t st, F8Args g) {
   }
   g.tiles_m = (g.M + BM - 1) / BM;
   g.tiles_n = (g.N + BN - 1) / BN;
-  hipLaunchKernelGGL(kfn, dim3(g.tiles_m * g.tiles_n), dim3(WGM * WGN * 64), lds, st, g);
+  hipLaunchKernelGGL(kfn, dim3(g.tiles_m * g.tiles_n, 1, ACC ? g.splits : 1), dim3(WGM * WGN * 64), lds, st, g);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
@@ -262,6 +291,14 @@ int f8_fwd(hipStream_t st, F8Args g) {
   switch (g.cfg) {
     case 0: return sl2::launch_f8<256, 256, 2, 2, 4>(st, g);
     case 1: return sl2::launch_f8<128, 128, 3, 2, 2>(st, g);
+    default: return -1;
+  }
+}
+
+int f8_accum(hipStream_t st, F8Args g) {
+  switch (g.cfg) {
+    case 0: return sl2::launch_f8<256, 256, 2, 2, 4, true>(st, g);
+    case 1: return sl2::launch_f8<128, 128, 3, 2, 2, true>(st, g);
     default: return -1;
   }
 }

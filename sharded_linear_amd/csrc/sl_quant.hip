@@ -1,0 +1,149 @@
+// MX quantisation of bf16 matrices for the all-MXFP8 step (gfx950).
+//
+// NVIDIA Megatron-Core guide "Generalized Tensor Parallelism", section 1.3: in the MXFP8 recipe
+// every GEMM of the step -- forward, dgrad and wgrad -- reads E4M3 elements with one E8M0 scale
+// per 32 elements along its own contraction axis, so a tensor consumed along both of its axes
+// (X, W, dY) is quantised twice: rowwise (blocks along the last axis) and columnwise (blocks down
+// the columns, stored transposed so that the consuming GEMM again reads k contiguously).  The
+// pages fix the block of 32 and the per-block scale; the conversion rule is the OCP MX v1.0 one:
+//   X = clamp(floor(log2 amax) - 8, -127, 127)   (8 = the largest E4M3 exponent), stored X + 127
+//   code(x) = E4M3 round-to-nearest-even of x / 2^X, saturating at +-448, sign kept
+//   an all-zero block stores scale 0 and zero codes.
+// Division by 2^X is a multiplication by an exact fp32 power of two (2^-127 is an fp32 subnormal,
+// still exact); an element so small that the product underflows rounds to a zero code either way.
+// The rounding works on the fp32 bit fields, so the codes do not depend on a conversion
+// instruction's rounding or saturation mode.
+//
+// One workgroup quantises a 128 x 128 tile: each thread takes two 32-element row blocks straight
+// from HBM (16-byte loads; four threads cover 256 contiguous bytes of a row) and, for the
+// columnwise copy, stages them in LDS, from which each thread then reads two 32-row column
+// blocks.  Every code store is 32 contiguous bytes; four column blocks of one tile make a whole
+// 128-byte row of the transposed output.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "sl_device.h"
+#include "sl_gemm_f8.h"
+
+namespace sl2 {
+
+// E4M3 code of v (finite, |v| < 512): the fp32 mantissa rounded to 3 bits, nearest-even, for
+// |v| >= 2^-6; a fixed step of 2^-9, nearest-even, below (code 8 is 2^-6 itself); 448 caps.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t ab = b & 0x7FFFFFFFu;
+  uint32_t code;
+  if (ab >= 0x3C800000u) {                                     // 2^-6
+    uint32_t r = (ab + 0x7FFFFu + ((ab >> 20) & 1u)) & 0xFFF00000u;
+    if (r > 0x43E00000u) r = 0x43E00000u;                      // 448
+    code = ((((r >> 23) & 0xFFu) - 120u) << 3) | ((r >> 20) & 7u);   // biased exponent 127 -> 7
+  } else {
+    code = uint32_t(__builtin_rintf(__uint_as_float(ab) * 512.0f));
+  }
+  return code | ((b >> 24) & 0x80u);
+}
+
+// Quantises 32 values: returns the biased scale and packs the codes into q[8] (little endian).
+__device__ __forceinline__ uint32_t mx_block(const float (&v)[32], uint32_t (&q)[8]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  if (amax == 0.f) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) q[w] = 0;
+    return 0;
+  }
+  int X = int((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 8;
+  X = X < -127 ? -127 : X > 127 ? 127 : X;
+  const float mult = -X >= -126 ? __uint_as_float(uint32_t(127 - X) << 23) : __uint_as_float(0x00400000u);
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) word |= e4m3_code(v[4 * w + e] * mult) << (8 * e);
+    q[w] = word;
+  }
+  return uint32_t(X + 127);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+constexpr int kQT = 128;                 // tile edge
+constexpr int kQStride = kQT + 8;        // LDS row stride (bf16 elements)
+
+template <bool ROWS, bool COLS>
+__global__ void __launch_bounds__(256) mx_quant_tile(const uint16_t* x, int64_t R, int64_t C, uint8_t* qr, uint8_t* sr,
+                                                      uint8_t* qc, uint8_t* sc) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[COLS ? kQT * kQStride : 1];
+  const int64_t r0 = int64_t(blockIdx.y) * kQT, c0 = int64_t(blockIdx.x) * kQT;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int idx = t + 256 * h, row = idx >> 2, blk = idx & 3;
+    const int64_t gr = r0 + row, gc = c0 + blk * 32;
+    const bool valid = gr < R && gc < C;          // a whole row block (rowwise copies: C % 32 == 0)
+    uint4 raw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)                    // 8-element chunks (C % 8 == 0): all or nothing
+      raw[k] = (gr < R && gc + 8 * k + 8 <= C) ? reinterpret_cast<const uint4*>(x + gr * C + gc)[k]
+                                               : make_uint4(0, 0, 0, 0);
+    if constexpr (COLS) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) reinterpret_cast<uint4*>(tile + row * kQStride + blk * 32)[k] = raw[k];
+    }
+    if constexpr (ROWS) {
+      if (valid) {
+        float v[32];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[8 * k + 2 * e] = bf16_lo(w[e]);
+            v[8 * k + 2 * e + 1] = bf16_hi(w[e]);
+          }
+        }
+        uint32_t q[8];
+        const uint32_t s = mx_block(v, q);
+        uint4* dst = reinterpret_cast<uint4*>(qr + gr * C + gc);
+        dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+        dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+        sr[gr * (C / 32) + gc / 32] = uint8_t(s);
+      }
+    }
+  }
+  if constexpr (COLS) {
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int idx = t + 256 * h, col = idx & (kQT - 1), rb = idx >> 7;
+      const int64_t gc = c0 + col, gr = r0 + rb * 32;
+      if (gc < C && gr < R) {
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = __uint_as_float(uint32_t(tile[(rb * 32 + i) * kQStride + col]) << 16);
+        uint32_t q[8];
+        const uint32_t s = mx_block(v, q);
+        uint4* dst = reinterpret_cast<uint4*>(qc + gc * R + gr);
+        dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+        dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+        sc[gc * (R / 32) + gr / 32] = uint8_t(s);
+      }
+    }
+  }
+}
+
+}  // namespace sl2
+
+int mx_quantize(hipStream_t st, const void* x, int64_t R, int64_t C, uint8_t* qr, uint8_t* sr, uint8_t* qc,
+                uint8_t* sc) {
+  if (R == 0 || C == 0 || (!qr && !qc)) return 0;
+  const dim3 grid(unsigned((C + sl2::kQT - 1) / sl2::kQT), unsigned((R + sl2::kQT - 1) / sl2::kQT));
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  if (qr && qc) hipLaunchKernelGGL((sl2::mx_quant_tile<true, true>), grid, dim3(256), 0, st, xp, R, C, qr, sr, qc, sc);
+  else if (qr) hipLaunchKernelGGL((sl2::mx_quant_tile<true, false>), grid, dim3(256), 0, st, xp, R, C, qr, sr, qc, sc);
+  else hipLaunchKernelGGL((sl2::mx_quant_tile<false, true>), grid, dim3(256), 0, st, xp, R, C, qr, sr, qc, sc);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}

@@ -170,3 +170,71 @@ def sl_linear_wgrad_accum_mxfp8x(Xq, Xs, dY, main_grad, workspace=None):
     check("sl_linear_wgrad_accum_mxfp8x", lib().sl_linear_wgrad_accum_mxfp8x(
         _stream(dev), _ptr(Xq), _ptr(Xs), _ptr(dY), _ptr(main_grad), T, n_in, n_out, _ptr(workspace), nbytes))
     return main_grad
+
+
+# ---- all-MXFP8 step ---------------------------------------------------------------------------
+
+def sl_mxfp8_quantize(x, rows=True, cols=True, out=None):
+    """MX-quantise bf16 x[R, C]: returns (q_rows, s_rows, q_cols, s_cols); a copy not asked for is
+    None.  Rowwise blocks run along C ([R, C] codes, [R, C/32] scales); columnwise blocks run down
+    the columns and are stored transposed ([C, R] codes, [C, R/32] scales).  ``out`` may supply
+    the four tensors."""
+    dev = _device(x)
+    R, C = x.shape
+    _want(x, "x", BF16, (R, C), dev)
+    if out is None:
+        out = (torch.empty((R, C), dtype=U8, device=dev) if rows else None,
+               torch.empty((R, C // 32), dtype=U8, device=dev) if rows else None,
+               torch.empty((C, R), dtype=U8, device=dev) if cols else None,
+               torch.empty((C, R // 32), dtype=U8, device=dev) if cols else None)
+    qr, sr, qc, sc = out
+    if qr is not None:
+        _want(qr, "q_rows", U8, (R, C), dev)
+        _want(sr, "s_rows", U8, (R, C // 32), dev)
+    if qc is not None:
+        _want(qc, "q_cols", U8, (C, R), dev)
+        _want(sc, "s_cols", U8, (C, R // 32), dev)
+    check("sl_mxfp8_quantize", lib().sl_mxfp8_quantize(
+        _stream(dev), _ptr(x), R, C, _ptr(qr), _ptr(sr), _ptr(qc), _ptr(sc)))
+    return qr, sr, qc, sc
+
+
+def sl_linear_dgrad_mxfp8(dYq, dYs, WqT, WsT, dX=None):
+    """dX[T,in] = deq(dYq, dYs)[T,out] . deq(WqT, WsT)[in,out]^T (bf16 out)."""
+    dev = _device(dYq)
+    T, n_out = dYq.shape
+    n_in = WqT.shape[0]
+    _want(dYq, "dYq", U8, (T, n_out), dev)
+    _want(dYs, "dYs", U8, (T, n_out // 32), dev)
+    _want(WqT, "WqT", U8, (n_in, n_out), dev)
+    _want(WsT, "WsT", U8, (n_in, n_out // 32), dev)
+    if dX is None:
+        dX = torch.empty((T, n_in), dtype=BF16, device=dev)
+    _want(dX, "dX", BF16, (T, n_in), dev)
+    check("sl_linear_dgrad_mxfp8", lib().sl_linear_dgrad_mxfp8(
+        _stream(dev), _ptr(dYq), _ptr(dYs), _ptr(WqT), _ptr(WsT), _ptr(dX), T, n_in, n_out))
+    return dX
+
+
+def sl_mxfp8_wgrad_workspace_bytes(T: int, n_in: int, n_out: int) -> int:
+    return int(lib().sl_mxfp8_wgrad_workspace_bytes(T, n_in, n_out))
+
+
+def sl_linear_wgrad_accum_mxfp8(dYqT, dYsT, XqT, XsT, main_grad, workspace=None):
+    """main_grad[out,in] += deq(dYqT, dYsT)[out,T] . deq(XqT, XsT)[in,T]^T in fp32, in place."""
+    dev = _device(dYqT)
+    n_out, T = dYqT.shape
+    n_in = XqT.shape[0]
+    _want(dYqT, "dYqT", U8, (n_out, T), dev)
+    _want(dYsT, "dYsT", U8, (n_out, T // 32), dev)
+    _want(XqT, "XqT", U8, (n_in, T), dev)
+    _want(XsT, "XsT", U8, (n_in, T // 32), dev)
+    _want(main_grad, "main_grad", F32, (n_out, n_in), dev)
+    need = sl_mxfp8_wgrad_workspace_bytes(T, n_in, n_out)
+    if workspace is None:
+        workspace = wgrad_workspace(dev, need) if need else None
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check("sl_linear_wgrad_accum_mxfp8", lib().sl_linear_wgrad_accum_mxfp8(
+        _stream(dev), _ptr(dYqT), _ptr(dYsT), _ptr(XqT), _ptr(XsT), _ptr(main_grad), T, n_in, n_out,
+        _ptr(workspace), nbytes))
+    return main_grad

@@ -25,6 +25,7 @@ class Workload:
     microbatches: int
     timed: tuple = ()              # params whose GEMMs form the step (default: all)
     mxfp8: bool = False            # W and X quantised to MXFP8, dY bf16
+    mxfp8_all: bool = False        # bf16 inputs, quantised to MXFP8 inside the step (all GEMMs fp8)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -53,6 +54,11 @@ WORKLOADS = {
     "c5": Workload("c5", 5, "Llama-3.2-1B-shape MLP TP=2 shard with MXFP8 W and X, 8 micro-batches",
                    {"linear_fc1": LLAMA1B_TP2["linear_fc1"], "linear_fc2": LLAMA1B_TP2["linear_fc2"]}, 8192, 8,
                    mxfp8=True),
+    # the next step of the low-precision path: every GEMM in MXFP8, dY quantised as well
+    "c6": Workload("c6", 6, "Llama-3.2-1B-shape MLP TP=2 shard, all GEMMs MXFP8 (X, W, dY quantised in the step), "
+                   "8 micro-batches",
+                   {"linear_fc1": LLAMA1B_TP2["linear_fc1"], "linear_fc2": LLAMA1B_TP2["linear_fc2"]}, 8192, 8,
+                   mxfp8_all=True),
 }
 
 

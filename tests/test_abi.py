@@ -93,6 +93,36 @@ def test_mxfp8_validation():
     assert L.sl_linear_fwd_mxfp8(None, None, None, None, None, None, 0, 64, 16) == SL_OK
 
 
+def test_all_mxfp8_validation():
+    """Argument checks of the quantiser and the both-MXFP8 dgrad / wgrad, host side only."""
+    L = _lib.lib()
+    q = L.sl_mxfp8_quantize
+    assert q(None, A, 64, 48, A, A, None, None) == SL_ESHAPE                      # cols % 32 (rows copy)
+    assert q(None, A, 48, 64, None, None, A, A) == SL_ESHAPE                      # rows % 32 (cols copy)
+    assert q(None, A, 64, 12, None, None, A, A) == SL_ESHAPE                      # cols % 8 (cols copy)
+    assert q(None, A, 64, 64, A, None, None, None) == SL_EINVAL                   # codes without scales
+    assert q(None, A, 64, 64, None, None, None, A) == SL_EINVAL
+    assert q(None, None, 64, 64, A, A, None, None) == SL_EINVAL
+    assert q(None, MIS, 64, 64, A, A, None, None) == SL_EALIGN
+    assert q(None, A, 64, 64, None, None, MIS, A) == SL_EALIGN
+    assert q(None, A, -1, 64, A, A, None, None) == SL_EINVAL
+    assert q(None, None, 0, 64, None, None, None, None) == SL_OK
+    d = L.sl_linear_dgrad_mxfp8
+    assert d(None, A, A, A, A, A, 16, 64, 96) == SL_ESHAPE                        # out % 128
+    assert d(None, A, A, A, None, A, 16, 64, 128) == SL_EINVAL
+    assert d(None, MIS, A, A, A, A, 16, 64, 128) == SL_EALIGN
+    w = L.sl_linear_wgrad_accum_mxfp8
+    assert w(None, A, A, A, A, A, 96, 64, 64, None, 0) == SL_ESHAPE               # T % 128
+    assert w(None, A, A, None, A, A, 128, 64, 64, None, 0) == SL_EINVAL
+    assert w(None, A, A, A, A, MIS, 128, 64, 64, None, 0) == SL_EALIGN
+    need = L.sl_mxfp8_wgrad_workspace_bytes(8192, 4096, 2048)                   # 128 tiles: split
+    assert need >= 2 * 2048 * 4096 * 4
+    assert w(None, A, A, A, A, A, 8192, 4096, 2048, None, 0) == SL_EWORKSPACE
+    assert w(None, A, A, A, A, A, 8192, 4096, 2048, A, need - 256) == SL_EWORKSPACE
+    assert L.sl_mxfp8_wgrad_workspace_bytes(8192, 2048, 8192) == 0              # 256 tiles: unsplit
+    assert L.sl_mxfp8_wgrad_workspace_bytes(100, 64, 64) == 0
+
+
 def test_zero_fill_validation():
     L = _lib.lib()
     assert L.sl_grad_buffer_zero(None, A, -1) == SL_EINVAL
