@@ -456,6 +456,9 @@ Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a
     // a K-major operand is half a cache line); dgrad, with one operand of each kind, the first
     // for long K and the second otherwise.
     if (cfg == 10) cfg = kind == Kind::Wgrad ? 15 : kind == Kind::Fwd ? 17 : (K >= 6144 ? 15 : 17);
+    // 256x128 tiles (shapes whose 256x256 tile count leaves CUs idle): the fixed-order 4-wave
+    // kernel with a 3-stage ring of 64 k, measured 20 % ahead of the compiler-scheduled one on dgrad
+    if (cfg == 3 && kind != Kind::Wgrad) cfg = 19;
   }
   Plan p = make_plan_cfg(kind, mxfp8, M, N, K, a_bytes, b_bytes, cfg);
   // configurations that prefill a deep ring need that many k stages in every split

@@ -17,7 +17,7 @@ struct Gemm2Args {
   int cfg;              // tile configuration, see gemm2_tile()
 };
 
-constexpr int kGemm2Configs = 19;
+constexpr int kGemm2Configs = 21;
 
 // A K-major (k contiguous) and B K-major: forward.
 int gemm2_fwd(hipStream_t st, Gemm2Args g);

@@ -392,9 +392,9 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
 // Barrier B(s+1), between the steps of stage s, certifies (i) every wave's loads of stage s + 1
 // have landed (each wave waits for its own with vmcnt first) and (ii) every wave has read all of
 // stage s (its second-step fragments were waited for), so its slot can take stage s + S.
-template <bool A_KM, bool B_KM, bool ACC, int S, int WGM, int WGN, int BK_>
+template <bool A_KM, bool B_KM, bool ACC, int S, int WGM, int WGN, int BK_, int BN_ = 256>
 struct G4 {
-  static constexpr int BM = 256, BN = 256, BK = BK_, WAVES = WGM * WGN, WM = BM / WGM, WN = BN / WGN;
+  static constexpr int BM = 256, BN = BN_, BK = BK_, WAVES = WGM * WGN, WM = BM / WGM, WN = BN / WGN;
   static constexpr int TM = WM / 32, TN = WN / 32;
   using OA = typename OpSel<A_KM, BM, BK>::T;
   using OB = typename OpSel<B_KM, BN, BK>::T;
@@ -443,9 +443,9 @@ __device__ __forceinline__ bf16x8 lds_rd_tr(uint32_t addr) {
 template <int N>
 __device__ __forceinline__ void asm_wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" : : "i"(N) : "memory"); }
 
-template <bool A_KM, bool B_KM, bool ACC, int S, int WGM, int WGN, int BK_>
+template <bool A_KM, bool B_KM, bool ACC, int S, int WGM, int WGN, int BK_, int BN_>
 __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
-  using P = G4<A_KM, B_KM, ACC, S, WGM, WGN, BK_>;
+  using P = G4<A_KM, B_KM, ACC, S, WGM, WGN, BK_, BN_>;
   using OA = typename P::OA;
   using OB = typename P::OB;
   constexpr int BK = P::BK, WAVES = P::WAVES, WM = P::WM, WN = P::WN, TM = P::TM, TN = P::TN;
@@ -650,10 +650,10 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-template <int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int BK = 32>
+template <int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int BK = 32, int BN = 256>
 int launch_g4(hipStream_t st, Gemm2Args g) {
-  using P = G4<A_KM, B_KM, ACC, S, WGM, WGN, BK>;
-  auto kfn = gemm4<A_KM, B_KM, ACC, S, WGM, WGN, BK>;
+  using P = G4<A_KM, B_KM, ACC, S, WGM, WGN, BK, BN>;
+  auto kfn = gemm4<A_KM, B_KM, ACC, S, WGM, WGN, BK, BN>;
   static bool attr = false;
   if (!attr) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, P::kLds) != hipSuccess)
@@ -694,6 +694,8 @@ int launch_g4(hipStream_t st, Gemm2Args g) {
 //  16: 256x256, BK 32, 4 stages, 8 waves 2x4 (128x64 wave tiles), fixed issue order     LDS 128 KiB
 //  17: 256x256, BK 64, 2 stages, 8 waves 2x4 (128x64 wave tiles), fixed issue order     LDS 128 KiB
 //  18: 256x256, BK 64, 2 stages, 4 waves (128x128 wave tiles), fixed issue order        LDS 128 KiB
+//  19: 256x128, BK 64, 3 stages, 4 waves (128x64 wave tiles), fixed issue order         LDS 144 KiB
+//  20: 256x128, BK 32, 4 stages, 4 waves (128x64 wave tiles), fixed issue order         LDS  96 KiB
 #define SL2_DISPATCH(AK, BKM, ACC)                                                                 \
   switch (g.cfg) {                                                                                 \
     case 0: return sl2::launch_cfg<256, 256, 32, 4, 2, 2, AK, BKM, ACC>(st, g);                   \
@@ -715,6 +717,8 @@ int launch_g4(hipStream_t st, Gemm2Args g) {
     case 16: return sl2::launch_g4<4, 2, 4, AK, BKM, ACC>(st, g);                                  \
     case 17: return sl2::launch_g4<2, 2, 4, AK, BKM, ACC, 64>(st, g);                              \
     case 18: return sl2::launch_g4<2, 2, 2, AK, BKM, ACC, 64>(st, g);                              \
+    case 19: return sl2::launch_g4<3, 2, 2, AK, BKM, ACC, 64, 128>(st, g);                         \
+    case 20: return sl2::launch_g4<4, 2, 2, AK, BKM, ACC, 32, 128>(st, g);                         \
     default: return -1;                                                                            \
   }
 
@@ -722,14 +726,16 @@ int gemm2_fwd(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, true, false) }
 int gemm2_dgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, false, false) }
 int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) }
 
-int gemm2_min_stages(int cfg) { return cfg == 15 || cfg == 16 ? 4 : cfg == 17 || cfg == 18 ? 2 : 1; }
+int gemm2_min_stages(int cfg) {
+  return cfg == 15 || cfg == 16 || cfg == 20 ? 4 : cfg == 17 || cfg == 18 ? 2 : cfg == 19 ? 3 : 1;
+}
 
 void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
-  *bk = (cfg == 0 || cfg == 7 || cfg == 8 || (cfg >= 12 && cfg <= 16)) ? 32 : 64;
+  *bk = (cfg == 0 || cfg == 7 || cfg == 8 || (cfg >= 12 && cfg <= 16) || cfg == 20) ? 32 : 64;
   static const int t[kGemm2Configs][2] = {
       {256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256}, {256, 256},
       {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {128, 256},
-      {256, 128}, {256, 256}, {256, 256}, {256, 256}, {256, 256}};
+      {256, 128}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {256, 128}};
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }

@@ -9,10 +9,13 @@
 //   X = clamp(floor(log2 amax) - 8, -127, 127)   (8 = the largest E4M3 exponent), stored X + 127
 //   code(x) = E4M3 round-to-nearest-even of x / 2^X, saturating at +-448, sign kept
 //   an all-zero block stores scale 0 and zero codes.
-// Division by 2^X is a multiplication by an exact fp32 power of two (2^-127 is an fp32 subnormal,
-// still exact); an element so small that the product underflows rounds to a zero code either way.
-// The rounding works on the fp32 bit fields, so the codes do not depend on a conversion
-// instruction's rounding or saturation mode.
+// The codes come from v_cvt_scalef32_pk_fp8_bf16, which divides two bf16 elements by an fp32
+// scale and rounds to E4M3, nearest-even, in one instruction.  Measured over every bf16 pattern
+// against the rule above (scales 2^-126 .. 2^100): identical, except that a quotient rounding past
+// 448 gives the NaN code S.1111.111 instead of saturating; those bytes are rewritten to S.1111.110
+// (448), the only change needed (E4M3 has no other NaN pattern).  A block whose shared exponent is
+// -127 (2^-127 is not a normal fp32 scale) takes a bit-field path instead: x times the exact fp32
+// power of two 2^127, rounded on the fp32 bit fields.  The GPU tests check every bf16 pattern.
 //
 // One workgroup quantises a 128 x 128 tile: each thread takes two 32-element row blocks straight
 // from HBM (16-byte loads; four threads cover 256 contiguous bytes of a row) and, for the
@@ -44,31 +47,56 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return code | ((b >> 24) & 0x80u);
 }
 
-// Quantises 32 values: returns the biased scale and packs the codes into q[8] (little endian).
-__device__ __forceinline__ uint32_t mx_block(const float (&v)[32], uint32_t (&q)[8]) {
-  float amax = 0.f;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Quantises one block of 32 bf16 elements, given as 16 words of two (element 2i in the low half of
+// word i): returns the biased scale and packs the codes into q[8] (code of element e in byte e).
+__device__ __forceinline__ uint32_t mx_block(const uint32_t (&w)[16], uint32_t (&q)[8]) {
+  // amax on the bit patterns: |bf16| orders like its 15-bit magnitude field
+  uint32_t m2 = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  if (amax == 0.f) {
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t a = w[i] & 0x7FFF7FFFu;
+    const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
+    const uint32_t mlo = m2 & 0xFFFFu, mhi = m2 >> 16;
+    m2 = (lo > mlo ? lo : mlo) | ((hi > mhi ? hi : mhi) << 16);
+  }
+  const uint32_t amax = (m2 & 0xFFFFu) > (m2 >> 16) ? (m2 & 0xFFFFu) : (m2 >> 16);   // bf16 bits
+  if (amax == 0) {
 #pragma unroll
-    for (int w = 0; w < 8; ++w) q[w] = 0;
+    for (int i = 0; i < 8; ++i) q[i] = 0;
     return 0;
   }
-  int X = int((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 8;
+  int X = int((amax >> 7) & 0xFFu) - 127 - 8;          // floor(log2 amax) - 8 (bf16 exponent field)
   X = X < -127 ? -127 : X > 127 ? 127 : X;
-  const float mult = -X >= -126 ? __uint_as_float(uint32_t(127 - X) << 23) : __uint_as_float(0x00400000u);
+  if (X > -127) {
+    const float scale = __uint_as_float(uint32_t(X + 127) << 23);
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t word = 0;
+    for (int i = 0; i < 8; ++i) {
+      s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16((s16x2){0, 0}, __builtin_bit_cast(bf16x2, w[2 * i]), scale, false);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, w[2 * i + 1]), scale, true);
+      uint32_t c = __builtin_bit_cast(uint32_t, r);
+      // quotients that rounded past 448 came back as the NaN code x.1111.111: saturate to x.1111.110
+      const uint32_t nan = ((c & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+      q[i] = c - (nan >> 7);
+    }
+  } else {
+    const float mult = __uint_as_float(0x7F000000u);     // 2^127, exact
 #pragma unroll
-    for (int e = 0; e < 4; ++e) word |= e4m3_code(v[4 * w + e] * mult) << (8 * e);
-    q[w] = word;
+    for (int i = 0; i < 8; ++i) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t h = w[2 * i + e / 2];
+        const float x = __uint_as_float((e & 1) ? (h & 0xFFFF0000u) : (h << 16));
+        word |= e4m3_code(x * mult) << (8 * e);
+      }
+      q[i] = word;
+    }
   }
   return uint32_t(X + 127);
 }
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 constexpr int kQT = 128;                 // tile edge
 constexpr int kQStride = kQT + 8;        // LDS row stride (bf16 elements)
@@ -95,15 +123,10 @@ __global__ void __launch_bounds__(256) mx_quant_tile(const uint16_t* x, int64_t 
     }
     if constexpr (ROWS) {
       if (valid) {
-        float v[32];
+        uint32_t v[16];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[8 * k + 2 * e] = bf16_lo(w[e]);
-            v[8 * k + 2 * e + 1] = bf16_hi(w[e]);
-          }
+          v[4 * k] = raw[k].x; v[4 * k + 1] = raw[k].y; v[4 * k + 2] = raw[k].z; v[4 * k + 3] = raw[k].w;
         }
         uint32_t q[8];
         const uint32_t s = mx_block(v, q);
@@ -121,9 +144,11 @@ __global__ void __launch_bounds__(256) mx_quant_tile(const uint16_t* x, int64_t 
       const int idx = t + 256 * h, col = idx & (kQT - 1), rb = idx >> 7;
       const int64_t gc = c0 + col, gr = r0 + rb * 32;
       if (gc < C && gr < R) {
-        float v[32];
+        uint32_t v[16];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = __uint_as_float(uint32_t(tile[(rb * 32 + i) * kQStride + col]) << 16);
+        for (int i = 0; i < 16; ++i)
+          v[i] = uint32_t(tile[(rb * 32 + 2 * i) * kQStride + col]) |
+                 (uint32_t(tile[(rb * 32 + 2 * i + 1) * kQStride + col]) << 16);
         uint32_t q[8];
         const uint32_t s = mx_block(v, q);
         uint4* dst = reinterpret_cast<uint4*>(qc + gc * R + gr);

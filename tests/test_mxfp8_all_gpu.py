@@ -58,6 +58,27 @@ def test_quantise_bit_exact(R, C):
     assert np.array_equal(qc.cpu().numpy(), wqc) and np.array_equal(sc.cpu().numpy(), wsc)
 
 
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_quantise_every_bf16_pattern(shuffle):
+    """Every finite bf16 bit pattern, laid out as a [2048, 32] matrix (in order, or shuffled so
+    that blocks mix magnitudes): rowwise and columnwise codes and scales bit for bit."""
+    say(f"case quantise every bf16 pattern shuffle={shuffle}")
+    pats = np.array([b for b in range(65536) if (b & 0x7F80) != 0x7F80], dtype=np.uint16)   # 65280
+    bits = np.zeros(2048 * 32, np.uint16)
+    bits[: pats.size] = np.random.default_rng(3).permutation(pats) if shuffle else pats
+    bits = bits.reshape(2048, 32)
+    xf = numerics.bf16_bits_to_f64(bits)
+    qr, sr, qc, sc = sl.sl_mxfp8_quantize(dev_bf16(bits))
+    torch.cuda.synchronize()
+    wqr, wsr = numerics.mx_quantize(xf)
+    wqc, wsc = numerics.mx_quantize_cols(xf)
+    assert np.array_equal(sr.cpu().numpy(), wsr) and np.array_equal(sc.cpu().numpy(), wsc)
+    got_r, got_c = qr.cpu().numpy(), qc.cpu().numpy()
+    bad = np.argwhere(got_r != wqr)[:5]
+    assert bad.size == 0, [(int(bits[r, c]), int(got_r[r, c]), int(wqr[r, c])) for r, c in bad]
+    assert np.array_equal(got_c, wqc)
+
+
 @pytest.mark.parametrize("R,C", [(64, 8), (160, 264)])
 def test_quantise_columnwise_only_ragged_cols(R, C):
     """Columnwise copies need only rows % 32 (and cols % 8)."""
