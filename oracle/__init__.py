@@ -14,7 +14,8 @@ Sources (web pages, cited by title and section):
   [GTP]       NVIDIA Megatron-Core developer guide, "Generalized Tensor Parallelism (GTP)"
 
 Modules:
-  numerics  decoding of bf16, E4M3 and E8M0 storage formats (pinned by closed-form tables)
+  numerics  decoding of bf16, E4M3, E8M0 and E2M1 storage formats and NVFP4 blocks (pinned by
+            closed-form tables and hand-decoded bytes); the MX quantiser
   linear    fwd / dgrad / fused wgrad-accumulate, brute-force twins for tiny shapes
   layout    the reverse-order, padded grad/param buffer layout
   shapes    parameter counts of the Llama-3.2-1B-shape ledger and its TP=2 shards

@@ -18,13 +18,14 @@ section 1 "Responsibilities of the two modules".
 
 All products are exact definitions, so the oracle computes them with a float64 matmul over the
 exact input values (bf16 widened).  The MXFP8 variants dequantise per 32-element block first,
-deq(q, s) = E4M3(q) * 2^(s-127), then apply the same formulas.
+deq(q, s) = E4M3(q) * 2^(s-127), then apply the same formulas; the NVFP4-weight variants decode
+deq(c, s, t) = E2M1(c) * E4M3(s) * t per 16-element block, t the fp32 per-tensor scale.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .numerics import bf16_bits_to_f64, mxfp8_dequant
+from .numerics import bf16_bits_to_f64, mxfp8_dequant, nvfp4_dequant
 
 
 def _f64(a):
@@ -164,3 +165,16 @@ def linear_wgrad_accum_mxfp8(main_grad, dYqT, dYsT, XqT, XsT):
     """main_grad + deq(dY columnwise) . deq(X columnwise)^T: both quantised along T and stored
     transposed ([out, T] and [in, T] codes)."""
     return np.asarray(main_grad, dtype=np.float64) + mxfp8_dequant(dYqT, dYsT) @ mxfp8_dequant(XqT, XsT).T
+
+
+# ---- NVFP4 weights ([GTP] section 1.3, "Native NVFP4 param": the weight shard lives as packed
+# E2M1 with block-16 scales and a per-tensor scale; activations and gradients stay bf16) ---------
+
+def linear_fwd_nvfp4w(X, Wq, Ws, w_scale):
+    """Y = X . deq(W)^T with W in NVFP4."""
+    return linear_fwd(X, nvfp4_dequant(Wq, Ws, w_scale))
+
+
+def linear_dgrad_nvfp4w(dY, Wq, Ws, w_scale):
+    """dX = dY . deq(W) with W in NVFP4."""
+    return linear_dgrad(dY, nvfp4_dequant(Wq, Ws, w_scale))

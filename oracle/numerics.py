@@ -9,6 +9,12 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 * E8M0 (the MX shared scale): an unsigned biased exponent, value 2^(e-127); 0xFF is NaN.
 * MX block size 32 along the contraction axis ([GTP] section 1.3, "Communication volume
   breakdown": one scale byte per 32 elements, 1/32 B per element).
+* E2M1 (the NVFP4 element, [GTP] section 1.3 "Native NVFP4 param": packed 4-bit kFloat4E2M1):
+  sign bit, 2 exponent bits with bias 1, 1 mantissa bit; exponent field 0 encodes the subnormal
+  0.5 * m; values 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Two codes per byte, element 2j in the low nibble.
+* NVFP4 ([GTP] section 1.3 table: block 16, 0.5 + 1/16 bytes per element, per-tensor scale set at
+  the optimizer-step quantize): deq = E2M1(code) * E4M3(block scale) * tensor scale (fp32); the
+  scale encodings are NVIDIA's NVFP4 definition, which the pages name but do not spell out.
 * MX quantisation (the pages fix only the block of 32 and per-block scaling with no tensor-wide
   amax, [GTP] section 1.3; the rule below is the OCP Microscaling v1.0 conversion): per block,
   shared exponent X = floor(log2 amax) - 8 (8 = the largest E4M3 exponent) clamped to
@@ -109,3 +115,30 @@ def mx_quantize_cols(x: np.ndarray, block: int = 32):
     result is stored transposed, codes [C, R] and scales [C, R/32] -- the layout in which a GEMM
     contracting over R reads it with k contiguous."""
     return mx_quantize(np.asarray(x, dtype=np.float64).T, block)
+
+
+def e2m1_value(code: int) -> float:
+    """Value of one E2M1 code by the definition (scalar, for tables and pins)."""
+    code = int(code) & 0xF
+    sign = -1.0 if code & 0x8 else 1.0
+    e, m = (code >> 1) & 0x3, code & 0x1
+    if e == 0:
+        return sign * 0.5 * m
+    return sign * (1.0 + 0.5 * m) * 2.0 ** (e - 1)
+
+
+E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def nvfp4_dequant(packed: np.ndarray, scales: np.ndarray, tensor_scale: float, block: int = 16) -> np.ndarray:
+    """deq = E2M1(code) * E4M3(scale) * tensor_scale for packed codes [rows, cols/2] (element 2j in
+    the low nibble of byte j) and E4M3 block scales [rows, cols/16]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    rows, half = packed.shape
+    codes = np.empty((rows, 2 * half), np.uint8)
+    codes[:, 0::2] = packed & 0xF
+    codes[:, 1::2] = packed >> 4
+    v = E2M1_TABLE[codes].reshape(rows, -1, block)
+    sc = e4m3_to_f64(scales)
+    assert sc.shape == (rows, 2 * half // block)
+    return (v * sc[..., None]).reshape(rows, 2 * half) * float(np.float32(tensor_scale))

@@ -8,6 +8,8 @@ Storage formats produced:
   * bf16: numpy uint16 bit patterns, rounded from float32 draws with round-to-nearest-even.
   * MXFP8 (OCP Microscaling v1.0, E4M3 elements, E8M0 shared scale per 32-element block along
     the last axis): uint8 element codes plus uint8 biased scale exponents, one per block.
+  * NVFP4 (E2M1 elements packed two per byte, element 2j in the low nibble; one E4M3 scale per
+    16-element block along the last axis; one fp32 per-tensor scale).
 
 Seeding recipe: numpy Generator(PCG64(seed)) with
     seed = 1000*config + 100*param_index + 10*microbatch + role,    role: W=0, X=1, dY=2,
@@ -120,3 +122,56 @@ def mxfp8_quantize(x: np.ndarray):
 def mxfp8_normal(shape, seed: int, std: float = 1.0):
     """N(0, std^2) float32 draws quantised to MXFP8 (codes, scales)."""
     return mxfp8_quantize(normal_f32(shape, seed, std))
+
+
+# E2M1 magnitudes by code 0..7 (sign in bit 3)
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def _e4m3_rne_codes(v: np.ndarray) -> np.ndarray:
+    """Non-negative float64 values -> E4M3 codes, round-to-nearest-even on the code grid,
+    saturating at 448 (the grid is increasing in the code for codes 0x00..0x7E)."""
+    grid = np.array([_e4m3_value(c) for c in range(0x7F)])
+    v = np.minimum(v, 448.0)
+    hi = np.clip(np.searchsorted(grid, v, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    dlo, dhi = np.abs(v - grid[lo]), np.abs(grid[hi] - v)
+    return np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi))).astype(np.uint8)
+
+
+def _e4m3_value(c: int) -> float:
+    e, m = (c >> 3) & 0xF, c & 7
+    return (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def nvfp4_quantize(x: np.ndarray):
+    """Quantise float32 ``x`` [rows, cols] (cols a multiple of 16) to NVFP4 with NVIDIA's recipe:
+    tensor scale t = amax / (6 * 448) (fp32); per 16-element block the E4M3 scale s = RNE(block
+    amax / 6 / t); elements x / (s t) rounded to nearest-even on the E2M1 grid, saturating at 6.
+    Returns (packed codes uint8 [rows, cols/2], scales uint8 [rows, cols/16], t as a Python float).
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    rows, cols = x.shape
+    if cols % 16:
+        raise ValueError("cols must be a multiple of 16")
+    amax = float(np.abs(x).max())
+    t = float(np.float32(amax / (6.0 * 448.0))) if amax > 0 else 1.0
+    xb = x.reshape(rows, cols // 16, 16)
+    bmax = np.abs(xb).max(axis=-1)
+    sc = _e4m3_rne_codes(bmax / 6.0 / t)
+    sval = np.array([_e4m3_value(c) for c in range(0x7F)])[sc]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(sval[..., None] > 0, np.abs(xb) / (sval[..., None] * t), 0.0)
+    v = np.minimum(v, 6.0)
+    hi = np.clip(np.searchsorted(_E2M1_GRID, v, side="left"), 0, 7)
+    lo = np.clip(hi - 1, 0, 7)
+    dlo, dhi = np.abs(v - _E2M1_GRID[lo]), np.abs(_E2M1_GRID[hi] - v)
+    mag = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    codes = (mag | np.where(np.signbit(xb) & (mag > 0), 8, 0)).astype(np.uint8).reshape(rows, cols)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sc.reshape(rows, cols // 16), t
+
+
+def nvfp4_normal(shape, seed: int, std: float = 1.0):
+    """N(0, std^2) float32 draws quantised to NVFP4 (packed codes, scales, tensor scale)."""
+    return nvfp4_quantize(normal_f32(shape, seed, std))

@@ -473,3 +473,93 @@ def test_mxfp8_backward_products_brute_force(T, n_in, n_out):
     G = linear.linear_wgrad_accum_mxfp8(G0, dYqT, dYsT, XqT, XsT)
     want = linear.wgrad_accum_brute(G0, numerics.mxfp8_dequant(XqT, XsT).T, numerics.mxfp8_dequant(dYqT, dYsT).T)
     assert np.allclose(G, want, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# NVFP4 weights: E2M1 elements, E4M3 scales per 16 elements, one fp32 tensor scale
+# ---------------------------------------------------------------------------------------------
+
+def test_e2m1_table_values():
+    # OCP MX v1.0 FP4 E2M1: bias 1, max normal 6 (0.111), min normal 1, one subnormal 0.5;
+    # no infinities or NaN; the 16 codes give 15 distinct values (+0 and -0).
+    t = numerics.E2M1_TABLE
+    assert list(t[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert np.array_equal(t[8:], -t[:8]) and math.copysign(1, t[8]) == -1
+    assert np.all(np.isfinite(t))
+
+
+def test_nvfp4_dequant_hand_worked_bytes():
+    """Two rows of 32 elements with hand-decoded bytes: nibble order (element 2j low), scale per
+    16-element block, E4M3 scale decode and the tensor scale."""
+    packed = np.zeros((2, 16), np.uint8)
+    packed[0, 0] = 0x21      # elements 0, 1 -> codes 1 (0.5), 2 (1.0)
+    packed[0, 7] = 0xF7      # elements 14, 15 -> codes 7 (6.0), 15 (-6.0)
+    packed[0, 8] = 0x9C      # elements 16, 17 -> codes 12 (-2.0), 9 (-0.5)
+    packed[1, 15] = 0x53     # elements 30, 31 -> codes 3 (1.5), 5 (3.0)
+    scales = np.array([[0x38, 0x40],       # 1.0, 2.0
+                       [0x01, 0x7E]],      # 2^-9 (smallest subnormal), 448
+                      np.uint8)
+    d = numerics.nvfp4_dequant(packed, scales, 0.25)
+    want = np.zeros((2, 32))
+    want[0, 0], want[0, 1], want[0, 14], want[0, 15] = 0.5 * 0.25, 1.0 * 0.25, 6.0 * 0.25, -6.0 * 0.25
+    want[0, 16], want[0, 17] = -2.0 * 2.0 * 0.25, -0.5 * 2.0 * 0.25
+    want[1, 30], want[1, 31] = 1.5 * 448 * 0.25, 3.0 * 448 * 0.25
+    assert np.array_equal(d, want)
+
+
+def test_nvfp4_tensor_scale_is_fp32():
+    # the per-tensor scale is an fp32 value: a float64 argument is taken after rounding to fp32
+    packed = np.full((1, 8), 0x22, np.uint8)               # every element 1.0
+    d = numerics.nvfp4_dequant(packed, np.array([[0x38]], np.uint8), 0.1)
+    assert np.all(d == float(np.float32(0.1)))
+
+
+def test_nvfp4_products_are_exact_in_bf16():
+    """Every E2M1 x E4M3 product (finite scale codes) has at most 6 significant bits and lies in
+    [2^-10, 2688], so it is a bf16 value: the unscaled weight needs no rounding."""
+    for sc in range(256):
+        s = numerics.e4m3_value(sc)
+        if not np.isfinite(s):
+            continue
+        for c in range(16):
+            p = numerics.e2m1_value(c) * s
+            b = synth.f32_to_bf16_bits(np.array([p], np.float32))
+            assert numerics.bf16_bits_to_f64(b)[0] == p
+
+
+def test_nvfp4_synthetic_weights_round_trip_bound():
+    """The input generator's NVFP4 encoding: codes decode to within half a grid step (at most one
+    E2M1 unit) of each scaled element, or 1/16 of the block maximum where the scale rounded down
+    and the element saturated at 6."""
+    x = synth.normal_f32((48, 160), 7, 0.02)
+    q, s, t = synth.nvfp4_quantize(x)
+    assert q.shape == (48, 80) and s.shape == (48, 10) and np.float32(t) == t
+    d = numerics.nvfp4_dequant(q, s, t)
+    sv = numerics.e4m3_to_f64(s) * t
+    bmax = np.abs(x.astype(np.float64)).reshape(48, 10, 16).max(-1)
+    bound = np.maximum(sv, bmax / 16.0) * (1 + 1e-6)
+    err = np.abs(d - x).reshape(48, 10, 16).max(-1)
+    assert np.all(err <= bound)
+    assert np.abs(d).max() <= 6 * 448 * t * (1 + 1e-6)
+
+
+@pytest.mark.parametrize("T,n_in,n_out", [(3, 16, 5), (7, 48, 2), (2, 32, 17)])
+def test_nvfp4_weight_products_brute_force(T, n_in, n_out):
+    """Forward and dgrad over an NVFP4 weight equal triple loops over weights decoded one element
+    at a time with the scalar E2M1 and E4M3 rules."""
+    rng = np.random.default_rng(T * 7 + n_in + n_out)
+    packed = rng.integers(0, 256, (n_out, n_in // 2), dtype=np.uint8)
+    scales = rng.integers(0x20, 0x50, (n_out, n_in // 16), dtype=np.uint8)
+    t = 0.0625
+    W = np.empty((n_out, n_in))
+    for o in range(n_out):
+        for i in range(n_in):
+            byte = int(packed[o, i // 2])
+            code = (byte >> 4) if i % 2 else (byte & 0xF)
+            W[o, i] = numerics.e2m1_value(code) * numerics.e4m3_value(int(scales[o, i // 16])) * t
+    X = synth.f32_to_bf16_bits(rng.standard_normal((T, n_in)).astype(np.float32))
+    dY = synth.f32_to_bf16_bits(rng.standard_normal((T, n_out)).astype(np.float32))
+    np.testing.assert_allclose(linear.linear_fwd_nvfp4w(X, packed, scales, t),
+                               linear.fwd_brute(numerics.bf16_bits_to_f64(X), W), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(linear.linear_dgrad_nvfp4w(dY, packed, scales, t),
+                               linear.dgrad_brute(numerics.bf16_bits_to_f64(dY), W), rtol=1e-12, atol=1e-12)
