@@ -8,7 +8,7 @@ GEMM) of K timed steps with one HIP event per step boundary; a second pass of K 
 every kernel launch with HIP events on the launch stream to give the per-kernel roofline
 figures (those events slow the step, so they stay out of the headline pass).
 
-    python bench.py [--steps K] [--warmup W] [--config c2|c1|c3|c4|c5] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config c2|c1|c3|c4|c5|c6|c7] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -131,6 +131,10 @@ def main():
         wt = configs.weight(w, n)
         if w.mxfp8:
             wq[n] = (dev_u8(wt[0]), dev_u8(wt[1]))
+        elif w.nvfp4w:
+            # the NVFP4 shard (packed codes, block scales, tensor scale); the param buffer's bf16
+            # view receives its materialisation once per step
+            wq[n] = (dev_u8(wt[0]), dev_u8(wt[1]), wt[2])
         else:
             buf.param(n).copy_(dev_bf16(wt))
     xs, dys = [], []
@@ -184,6 +188,8 @@ def main():
         launch("zero", 0, sl.sl_grad_buffer_zero, buf.grad_data, timed=timed)
         if w.mxfp8_all:
             return step_mxfp8_all(timed)
+        if w.nvfp4w:
+            return step_nvfp4w(timed)
         for k in range(w.microbatches):
             for n in names:
                 o, i = w.params[n]
@@ -225,6 +231,24 @@ def main():
                 launch("wgrad", 2 * T * i * o, sl.sl_linear_wgrad_accum_mxfp8, dYqT, dYsT, XqT, XsT,
                        buf.main_grad(n), wss[n], timed=timed)
 
+    def step_nvfp4w(timed):
+        # NVFP4 weights materialised once per step (exact bf16 products E2M1 x E4M3); every
+        # micro-batch's fwd and dgrad read them with the fp32 tensor scale in the epilogue
+        for n in names:
+            launch("materialize", 0, sl.sl_nvfp4_materialize, wq[n][0], wq[n][1], buf.param(n), timed=timed)
+        for k in range(w.microbatches):
+            for n in names:
+                o, i = w.params[n]
+                launch("fwd", 2 * T * i * o, sl.sl_linear_fwd_nvfp4w, xs[k][n], buf.param(n), wq[n][2], ys[n],
+                       timed=timed)
+            for n in reversed(names):
+                o, i = w.params[n]
+                f = 2 * T * i * o
+                launch("dgrad", f, sl.sl_linear_dgrad_nvfp4w, dys[k][n], buf.param(n), wq[n][2], dxs[n],
+                       timed=timed)
+                launch("wgrad", f, sl.sl_linear_wgrad_accum, xs[k][n], dys[k][n], buf.main_grad(n), wss[n],
+                       timed=timed)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -248,7 +272,8 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     # MXFP8 workload: fwd runs block-scaled fp8 MFMA, dgrad/wgrad bf16 MFMA on the exactly
     # dequantised operand; the bf16 peak is the conservative denominator for the whole step.
-    dtype = "mxfp8-e4m3 fwd / bf16 bwd" if w.mxfp8 else "mxfp8-e4m3" if w.mxfp8_all else "bf16"
+    dtype = ("mxfp8-e4m3 fwd / bf16 bwd" if w.mxfp8 else "mxfp8-e4m3" if w.mxfp8_all else
+             "bf16 (nvfp4 weights)" if w.nvfp4w else "bf16")
     peak = PEAK_TFLOPS["fp8"] if w.mxfp8_all else PEAK_TFLOPS["bf16"]
     med = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
 
@@ -293,7 +318,9 @@ def main():
                    "flops_per_step": flops, "step": "zero grad_data; per micro-batch: fwd of each "
                    "shard, then dgrad + fused fp32 wgrad-accumulate in backward order" +
                    ("; W quantised once per step, X before fwd and dY before dgrad, each rowwise and "
-                    "columnwise (MXFP8 quantisation kernels inside the timed step)" if w.mxfp8_all else "")},
+                    "columnwise (MXFP8 quantisation kernels inside the timed step)" if w.mxfp8_all else
+                    "; NVFP4 weights materialised to bf16 once per step (inside the timed step), fwd and "
+                    "dgrad scaled by the fp32 tensor scale" if w.nvfp4w else "")},
         "frac_of_peak": round(tflops / peak, 4),
         "step_ms": {"median": round(med, 4), "min": round(step_ms[0], 4), "max": round(step_ms[-1], 4),
                     "tflops_at_median": round(flops / (med * 1e-3) / 1e12, 2),
@@ -320,6 +347,7 @@ def cpu_baseline(w):
     same workload until about 10 s have passed."""
     import numpy as np
     from oracle import linear as ol
+    from oracle import numerics
     from synth import configs
 
     try:
@@ -336,6 +364,9 @@ def cpu_baseline(w):
     done_flops, elapsed, mbs = 0, 0.0, 0
     if w.mxfp8_all:
         return cpu_baseline_mxfp8_all(w, names, weights, cores, host)
+    if w.nvfp4w:
+        log("cpu baseline: NVFP4-weight workload, oracle decodes the weight once")
+        weights = {n: numerics.nvfp4_dequant(*weights[n]) for n in names}
     for k in range(w.microbatches):
         xk = {n: configs.x(w, n, k) for n in names}
         dyk = {n: configs.dy(w, n, k) for n in names}

@@ -180,6 +180,34 @@ int sl_linear_wgrad_accum_mxfp8(void* stream, const uint8_t* dYqT, const uint8_t
                                 int64_t T, int64_t in, int64_t out, void* workspace,
                                 size_t workspace_bytes);
 
+/* ---- NVFP4 weights -------------------------------------------------------------------------
+ * NVIDIA Megatron-Core guide "Generalized Tensor Parallelism", section 1.3 (native NVFP4 param):
+ * the weight shard W[out, in] is kept as NVFP4 -- packed 4-bit E2M1 codes, one E4M3 scale per
+ * 16 elements along in, and one fp32 per-tensor scale t (set when the optimizer writes the
+ * shard) -- and activations and gradients stay bf16:
+ *   deq(W)[o][i] = E2M1(code[o][i]) * E4M3(scale[o][i/16]) * t
+ *   forward: Y  = X . deq(W)^T          dgrad: dX = dY . deq(W)
+ * (the weight gradient does not read W: sl_linear_wgrad_accum applies unchanged).
+ *
+ * sl_nvfp4_materialize: Wq[rows, cols/2] packed codes (element 2j of a row in the low nibble of
+ * byte j) and Ws[rows, cols/16] E4M3 scale bytes into Wm[rows, cols] bf16 holding
+ * E2M1(code) * E4M3(scale) -- exact, since every such product is a bf16 value; t is NOT applied.
+ * cols % 16 == 0 (the NVFP4 alignment pad; SL_ESHAPE otherwise); Wq and Wm 16-byte aligned
+ * (SL_EALIGN); the caller owns all three buffers.  A NaN scale byte (S.1111.111) gives NaN
+ * weights.  Materialise once per optimizer step; every micro-batch's products reuse Wm.
+ *
+ * sl_linear_fwd_nvfp4w / sl_linear_dgrad_nvfp4w: as sl_linear_fwd / sl_linear_dgrad with W = Wm
+ * from sl_nvfp4_materialize and w_scale = t: the fp32 accumulators are multiplied by w_scale
+ * before the bf16 rounding of Y or dX.  in % 16 == 0 (SL_ESHAPE); w_scale must be finite
+ * (SL_EINVAL); the other rules are those of the bf16 entry points.
+ * ------------------------------------------------------------------------------------------- */
+int sl_nvfp4_materialize(void* stream, const uint8_t* Wq, const uint8_t* Ws, void* Wm, int64_t rows,
+                         int64_t cols);
+int sl_linear_fwd_nvfp4w(void* stream, const void* X, const void* Wm, float w_scale, void* Y,
+                         int64_t T, int64_t in, int64_t out);
+int sl_linear_dgrad_nvfp4w(void* stream, const void* dY, const void* Wm, float w_scale, void* dX,
+                           int64_t T, int64_t in, int64_t out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libsharded_linear.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("sl_gemm.hip", "sl_gemm2.hip", "sl_gemm_f8.hip", "sl_quant.hip", "sl_layout.cpp")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("sl_gemm.hip", "sl_gemm2.hip", "sl_gemm_f8.hip", "sl_quant.hip", "sl_nvfp4.hip", "sl_layout.cpp")]
 ARCH = os.environ.get("SL_OFFLOAD_ARCH", "gfx950")
 
 

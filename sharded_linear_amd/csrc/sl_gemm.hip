@@ -27,6 +27,7 @@
 // of main_grad.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -63,6 +64,7 @@ struct Args {
   int tiles_m, tiles_n;
   int splits, kt_per_split;
   float* ws;            // split-K partial planes [splits][M][N]
+  float alpha = 1.0f;   // bf16 results are alpha * (A . B^T), scaled in fp32 before rounding
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -295,7 +297,7 @@ gemm_kernel(Args args) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + row_in_blk + (r & 3);
-          if (m < args.M && n < args.N) C[int64_t(m) * args.ldc + n] = static_cast<__bf16>(acc[i][j][r]);
+          if (m < args.M && n < args.N) C[int64_t(m) * args.ldc + n] = static_cast<__bf16>(acc[i][j][r] * args.alpha);
         }
       }
   } else {
@@ -508,6 +510,7 @@ int run_v2(hipStream_t st, Kind kind, const Args& a, const Plan& p, int64_t a_by
   g.splits = a.splits; g.kt_per_split = a.kt_per_split;
   g.ws = a.ws;
   g.cfg = p.cfg;
+  g.alpha = a.alpha;
   const int r = kind == Kind::Fwd ? gemm2_fwd(st, g) : kind == Kind::Dgrad ? gemm2_dgrad(st, g) : gemm2_wgrad(st, g);
   return r == 0 ? SL_OK : SL_EHIP;
 }
@@ -541,6 +544,44 @@ Args base_args(int64_t M, int64_t N, int64_t K, const Plan& p) {
   return a;
 }
 
+// Y = alpha * (X . W^T) in bf16 (alpha = 1 for the plain product)
+int linear_fwd(hipStream_t hs, const void* X, const void* W, float alpha, void* Y, int64_t T, int64_t in,
+               int64_t out) {
+  int st = check_dims(T, in, out, 8);
+  if (st) return st;
+  if (T == 0 || out == 0) return SL_OK;
+  if (!Y || (in > 0 && (!X || !W))) return SL_EINVAL;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return SL_EALIGN;
+  const Plan p = make_plan(Kind::Fwd, false, T, out, in, T * in * 2, out * in * 2);
+  Args a = base_args(T, out, in, p);
+  a.a = {X, nullptr, in, int(T)};
+  a.b = {W, nullptr, in, int(out)};
+  a.c = Y;
+  a.ldc = out;
+  a.alpha = alpha;
+  if (p.v2) return run_v2(hs, Kind::Fwd, a, p, T * in * 2, out * in * 2);
+  return run_v1<true, true, Elem::BF16, Elem::BF16, Epi::StoreBF16>(hs, a, p);
+}
+
+// dX = alpha * (dY . W) in bf16
+int linear_dgrad(hipStream_t hs, const void* dY, const void* W, float alpha, void* dX, int64_t T, int64_t in,
+                 int64_t out) {
+  int st = check_dims(T, in, out, 8);
+  if (st) return st;
+  if (T == 0 || in == 0) return SL_OK;
+  if (!dX || (out > 0 && (!dY || !W))) return SL_EINVAL;
+  if (!aligned16(dY) || !aligned16(W) || !aligned16(dX)) return SL_EALIGN;
+  const Plan p = make_plan(Kind::Dgrad, false, T, in, out, T * out * 2, out * in * 2);
+  Args a = base_args(T, in, out, p);
+  a.a = {dY, nullptr, out, int(T)};
+  a.b = {W, nullptr, in, int(in)};
+  a.c = dX;
+  a.ldc = in;
+  a.alpha = alpha;
+  if (p.v2) return run_v2(hs, Kind::Dgrad, a, p, T * out * 2, out * in * 2);
+  return run_v1<true, false, Elem::BF16, Elem::BF16, Epi::StoreBF16>(hs, a, p);
+}
+
 }  // namespace
 
 extern "C" int sl_grad_buffer_zero(void* stream, float* grad_data, int64_t numel) {
@@ -560,38 +601,44 @@ extern "C" int sl_grad_buffer_zero(void* stream, float* grad_data, int64_t numel
 
 extern "C" int sl_linear_fwd(void* stream, const void* X, const void* W, void* Y, int64_t T, int64_t in,
                              int64_t out) {
-  int st = check_dims(T, in, out, 8);
-  if (st) return st;
-  if (T == 0 || out == 0) return SL_OK;
-  if (!Y || (in > 0 && (!X || !W))) return SL_EINVAL;
-  if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return SL_EALIGN;
-  const Plan p = make_plan(Kind::Fwd, false, T, out, in, T * in * 2, out * in * 2);
-  Args a = base_args(T, out, in, p);
-  a.a = {X, nullptr, in, int(T)};
-  a.b = {W, nullptr, in, int(out)};
-  a.c = Y;
-  a.ldc = out;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (p.v2) return run_v2(hs, Kind::Fwd, a, p, T * in * 2, out * in * 2);
-  return run_v1<true, true, Elem::BF16, Elem::BF16, Epi::StoreBF16>(hs, a, p);
+  return linear_fwd(static_cast<hipStream_t>(stream), X, W, 1.0f, Y, T, in, out);
 }
 
 extern "C" int sl_linear_dgrad(void* stream, const void* dY, const void* W, void* dX, int64_t T, int64_t in,
                                int64_t out) {
-  int st = check_dims(T, in, out, 8);
-  if (st) return st;
-  if (T == 0 || in == 0) return SL_OK;
-  if (!dX || (out > 0 && (!dY || !W))) return SL_EINVAL;
-  if (!aligned16(dY) || !aligned16(W) || !aligned16(dX)) return SL_EALIGN;
-  const Plan p = make_plan(Kind::Dgrad, false, T, in, out, T * out * 2, out * in * 2);
-  Args a = base_args(T, in, out, p);
-  a.a = {dY, nullptr, out, int(T)};
-  a.b = {W, nullptr, in, int(in)};
-  a.c = dX;
-  a.ldc = in;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (p.v2) return run_v2(hs, Kind::Dgrad, a, p, T * out * 2, out * in * 2);
-  return run_v1<true, false, Elem::BF16, Elem::BF16, Epi::StoreBF16>(hs, a, p);
+  return linear_dgrad(static_cast<hipStream_t>(stream), dY, W, 1.0f, dX, T, in, out);
+}
+
+// ---- NVFP4 weights ------------------------------------------------------------------------------
+// The weight shard is stored as NVFP4 (NVIDIA Megatron-Core guide "Generalized Tensor
+// Parallelism", section 1.3, native NVFP4 param): E2M1 codes, an E4M3 scale per 16 elements and
+// one fp32 tensor scale.  Every E2M1 x E4M3 product is a bf16 value, so the materialised weight
+// holds those products exactly and the tensor scale multiplies the fp32 accumulators before the
+// bf16 rounding of the result; the products themselves run on the bf16 kernels.
+
+extern "C" int sl_nvfp4_materialize(void* stream, const uint8_t* Wq, const uint8_t* Ws, void* Wm, int64_t rows,
+                                    int64_t cols) {
+  if (rows < 0 || cols < 0) return SL_EINVAL;
+  if (cols % 16) return SL_ESHAPE;
+  if (rows >= kMaxExtent || cols >= kMaxExtent) return SL_ESHAPE;
+  if (rows == 0 || cols == 0) return SL_OK;
+  if (!Wq || !Ws || !Wm) return SL_EINVAL;
+  if (!aligned16(Wq) || !aligned16(Wm)) return SL_EALIGN;
+  return nvfp4_expand(static_cast<hipStream_t>(stream), Wq, Ws, Wm, rows, cols) == 0 ? SL_OK : SL_EHIP;
+}
+
+extern "C" int sl_linear_fwd_nvfp4w(void* stream, const void* X, const void* Wm, float w_scale, void* Y,
+                                    int64_t T, int64_t in, int64_t out) {
+  if (!std::isfinite(w_scale)) return SL_EINVAL;
+  if (in % 16) return SL_ESHAPE;
+  return linear_fwd(static_cast<hipStream_t>(stream), X, Wm, w_scale, Y, T, in, out);
+}
+
+extern "C" int sl_linear_dgrad_nvfp4w(void* stream, const void* dY, const void* Wm, float w_scale, void* dX,
+                                      int64_t T, int64_t in, int64_t out) {
+  if (!std::isfinite(w_scale)) return SL_EINVAL;
+  if (in % 16) return SL_ESHAPE;
+  return linear_dgrad(static_cast<hipStream_t>(stream), dY, Wm, w_scale, dX, T, in, out);
 }
 
 extern "C" size_t sl_wgrad_workspace_bytes(int64_t T, int64_t in, int64_t out) {

@@ -15,6 +15,7 @@ struct Gemm2Args {
   int splits, kt_per_split;
   float* ws;            // split-K partial planes [splits][M][N] (accumulating kernel)
   int cfg;              // tile configuration, see gemm2_tile()
+  float alpha = 1.0f;   // bf16 results are alpha * (A . B^T), scaled in fp32 before rounding
 };
 
 constexpr int kGemm2Configs = 21;

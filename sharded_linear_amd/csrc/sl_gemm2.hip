@@ -203,7 +203,7 @@ __device__ __forceinline__ void store_tile(const Gemm2Args& g, f32x16 (&acc)[TM]
         for (int q = 0; q < 4; ++q) {
           bf16x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(acc[i][j][4 * q + e]);
+          for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(acc[i][j][4 * q + e] * g.alpha);
           *reinterpret_cast<bf16x4*>(ep + E::off(i * 32 + rl, (j * 32 + 8 * q) / 8) + 8 * hl) = v;
         }
     __bf16* C = static_cast<__bf16*>(g.c);

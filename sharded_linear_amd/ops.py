@@ -238,3 +238,52 @@ def sl_linear_wgrad_accum_mxfp8(dYqT, dYsT, XqT, XsT, main_grad, workspace=None)
         _stream(dev), _ptr(dYqT), _ptr(dYsT), _ptr(XqT), _ptr(XsT), _ptr(main_grad), T, n_in, n_out,
         _ptr(workspace), nbytes))
     return main_grad
+
+
+# ---- NVFP4 weights ------------------------------------------------------------------------------
+
+def sl_nvfp4_materialize(Wq, Ws, Wm=None):
+    """Wm[rows, cols] (bf16) = E2M1(Wq) * E4M3(Ws) per 16-element block, exactly; the tensor scale
+    is not applied.  Wq [rows, cols/2] packed codes (element 2j in the low nibble of byte j),
+    Ws [rows, cols/16] scale bytes."""
+    dev = _device(Wq)
+    rows, half = Wq.shape
+    cols = 2 * half
+    _want(Wq, "Wq", U8, (rows, half), dev)
+    _want(Ws, "Ws", U8, (rows, cols // 16), dev)
+    if Wm is None:
+        Wm = torch.empty((rows, cols), dtype=BF16, device=dev)
+    _want(Wm, "Wm", BF16, (rows, cols), dev)
+    check("sl_nvfp4_materialize", lib().sl_nvfp4_materialize(
+        _stream(dev), _ptr(Wq), _ptr(Ws), _ptr(Wm), rows, cols))
+    return Wm
+
+
+def sl_linear_fwd_nvfp4w(X, Wm, w_scale: float, Y=None):
+    """Y[T,out] = w_scale * (X[T,in] . Wm[out,in]^T), scaled in fp32, rounded to bf16."""
+    dev = _device(X)
+    T, n_in = X.shape
+    n_out = Wm.shape[0]
+    _want(X, "X", BF16, (T, n_in), dev)
+    _want(Wm, "Wm", BF16, (n_out, n_in), dev)
+    if Y is None:
+        Y = torch.empty((T, n_out), dtype=BF16, device=dev)
+    _want(Y, "Y", BF16, (T, n_out), dev)
+    check("sl_linear_fwd_nvfp4w", lib().sl_linear_fwd_nvfp4w(
+        _stream(dev), _ptr(X), _ptr(Wm), float(w_scale), _ptr(Y), T, n_in, n_out))
+    return Y
+
+
+def sl_linear_dgrad_nvfp4w(dY, Wm, w_scale: float, dX=None):
+    """dX[T,in] = w_scale * (dY[T,out] . Wm[out,in]), scaled in fp32, rounded to bf16."""
+    dev = _device(dY)
+    T, n_out = dY.shape
+    n_in = Wm.shape[1]
+    _want(dY, "dY", BF16, (T, n_out), dev)
+    _want(Wm, "Wm", BF16, (n_out, n_in), dev)
+    if dX is None:
+        dX = torch.empty((T, n_in), dtype=BF16, device=dev)
+    _want(dX, "dX", BF16, (T, n_in), dev)
+    check("sl_linear_dgrad_nvfp4w", lib().sl_linear_dgrad_nvfp4w(
+        _stream(dev), _ptr(dY), _ptr(Wm), float(w_scale), _ptr(dX), T, n_in, n_out))
+    return dX

@@ -149,27 +149,34 @@ def nvfp4_quantize(x: np.ndarray):
     tensor scale t = amax / (6 * 448) (fp32); per 16-element block the E4M3 scale s = RNE(block
     amax / 6 / t); elements x / (s t) rounded to nearest-even on the E2M1 grid, saturating at 6.
     Returns (packed codes uint8 [rows, cols/2], scales uint8 [rows, cols/16], t as a Python float).
+    Works through 256-row chunks (large fresh arrays are slow to fault in).
     """
-    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    x = np.asarray(x, dtype=np.float32)
     rows, cols = x.shape
     if cols % 16:
         raise ValueError("cols must be a multiple of 16")
-    amax = float(np.abs(x).max())
+    amax = float(max(x.max(initial=0.0), -x.min(initial=0.0)))
     t = float(np.float32(amax / (6.0 * 448.0))) if amax > 0 else 1.0
-    xb = x.reshape(rows, cols // 16, 16)
-    bmax = np.abs(xb).max(axis=-1)
-    sc = _e4m3_rne_codes(bmax / 6.0 / t)
-    sval = np.array([_e4m3_value(c) for c in range(0x7F)])[sc]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        v = np.where(sval[..., None] > 0, np.abs(xb) / (sval[..., None] * t), 0.0)
-    v = np.minimum(v, 6.0)
-    hi = np.clip(np.searchsorted(_E2M1_GRID, v, side="left"), 0, 7)
-    lo = np.clip(hi - 1, 0, 7)
-    dlo, dhi = np.abs(v - _E2M1_GRID[lo]), np.abs(_E2M1_GRID[hi] - v)
-    mag = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
-    codes = (mag | np.where(np.signbit(xb) & (mag > 0), 8, 0)).astype(np.uint8).reshape(rows, cols)
-    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    return packed, sc.reshape(rows, cols // 16), t
+    packed = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 16), np.uint8)
+    svals = np.array([_e4m3_value(c) for c in range(0x7F)])
+    for r0 in range(0, rows, 256):
+        xb = x[r0:r0 + 256].astype(np.float64).reshape(-1, cols // 16, 16)
+        bmax = np.abs(xb).max(axis=-1)
+        sc = _e4m3_rne_codes(bmax / 6.0 / t)
+        sval = svals[sc]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            v = np.where(sval[..., None] > 0, np.abs(xb) / (sval[..., None] * t), 0.0)
+        # nearest E2M1 magnitude index, ties to the even index: count the midpoints below v (a
+        # midpoint whose upper neighbour has the even index counts when v reaches it)
+        mag = np.zeros(v.shape, np.uint8)
+        for mid, upper_even in ((0.25, False), (0.75, True), (1.25, False), (1.75, True),
+                                (2.5, False), (3.5, True), (5.0, False)):
+            mag += (v >= mid) if upper_even else (v > mid)
+        codes = (mag | ((np.signbit(xb) & (mag > 0)).astype(np.uint8) << 3)).reshape(-1, cols)
+        packed[r0:r0 + 256] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+        scales[r0:r0 + 256] = sc
+    return packed, scales, t
 
 
 def nvfp4_normal(shape, seed: int, std: float = 1.0):

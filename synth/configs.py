@@ -12,7 +12,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 
-from . import ROLE_DY, ROLE_W, ROLE_X, W_STD, mxfp8_normal, normal_bf16, seed_for
+from . import ROLE_DY, ROLE_W, ROLE_X, W_STD, mxfp8_normal, normal_bf16, nvfp4_normal, seed_for
 
 
 @dataclass(frozen=True)
@@ -26,6 +26,7 @@ class Workload:
     timed: tuple = ()              # params whose GEMMs form the step (default: all)
     mxfp8: bool = False            # W and X quantised to MXFP8, dY bf16
     mxfp8_all: bool = False        # bf16 inputs, quantised to MXFP8 inside the step (all GEMMs fp8)
+    nvfp4w: bool = False           # W stored as NVFP4 (packed E2M1, E4M3 per 16, fp32 tensor scale)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -59,6 +60,10 @@ WORKLOADS = {
                    "8 micro-batches",
                    {"linear_fc1": LLAMA1B_TP2["linear_fc1"], "linear_fc2": LLAMA1B_TP2["linear_fc2"]}, 8192, 8,
                    mxfp8_all=True),
+    # native NVFP4 weights: the shard stays NVFP4, activations and gradients bf16
+    "c7": Workload("c7", 7, "Llama-3.2-1B-shape MLP TP=2 shard with NVFP4 weights, 8 micro-batches",
+                   {"linear_fc1": LLAMA1B_TP2["linear_fc1"], "linear_fc2": LLAMA1B_TP2["linear_fc2"]}, 8192, 8,
+                   nvfp4w=True),
 }
 
 
@@ -67,9 +72,12 @@ def _pidx(w: Workload, name: str) -> int:
 
 
 def weight(w: Workload, name: str):
-    """bf16 bits [out, in], or (codes, scales) for MXFP8 workloads."""
+    """bf16 bits [out, in]; (codes, scales) for MXFP8 workloads; (packed codes, scales, tensor
+    scale) for NVFP4-weight workloads."""
     shape = w.params[name]
     seed = seed_for(w.index, _pidx(w, name), 0, ROLE_W)
+    if w.nvfp4w:
+        return nvfp4_normal(shape, seed, W_STD)
     return mxfp8_normal(shape, seed, W_STD) if w.mxfp8 else normal_bf16(shape, seed, W_STD)
 
 

@@ -123,6 +123,28 @@ def test_all_mxfp8_validation():
     assert L.sl_mxfp8_wgrad_workspace_bytes(100, 64, 64) == 0
 
 
+def test_nvfp4_validation():
+    """Argument checks of the NVFP4 materialiser and the scaled bf16 products, host side only."""
+    L = _lib.lib()
+    m = L.sl_nvfp4_materialize
+    assert m(None, A, A, A, 64, 24) == SL_ESHAPE                                  # cols % 16
+    assert m(None, A, A, A, -1, 32) == SL_EINVAL
+    assert m(None, None, A, A, 64, 32) == SL_EINVAL
+    assert m(None, A, None, A, 64, 32) == SL_EINVAL
+    assert m(None, MIS, A, A, 64, 32) == SL_EALIGN
+    assert m(None, A, A, MIS, 64, 32) == SL_EALIGN
+    assert m(None, None, None, None, 0, 32) == SL_OK
+    assert m(None, None, None, None, 64, 0) == SL_OK
+    for f in (L.sl_linear_fwd_nvfp4w, L.sl_linear_dgrad_nvfp4w):
+        assert f(None, A, A, float("nan"), A, 16, 64, 64) == SL_EINVAL
+        assert f(None, A, A, float("inf"), A, 16, 64, 64) == SL_EINVAL
+        assert f(None, A, A, 1.0, A, 16, 40, 64) == SL_ESHAPE                     # in % 16
+        assert f(None, A, A, 1.0, A, 16, 64, 12) == SL_ESHAPE                     # out % 8
+        assert f(None, MIS, A, 1.0, A, 16, 64, 64) == SL_EALIGN
+        assert f(None, A, None, 1.0, A, 16, 64, 64) == SL_EINVAL
+        assert f(None, None, None, 1.0, None, 0, 64, 64) == SL_OK
+
+
 def test_zero_fill_validation():
     L = _lib.lib()
     assert L.sl_grad_buffer_zero(None, A, -1) == SL_EINVAL

@@ -1,0 +1,148 @@
+"""GPU parity of the NVFP4-weight path (through the C ABI) against the float64 oracle.
+
+Materialisation is byte work with an exact result (every E2M1 x E4M3 product is a bf16 value), so
+it is compared bit for bit with the oracle's decode; the forward and dgrad products over the
+materialised weight and the fp32 tensor scale are compared with the oracle's products,
+max|gpu - ref| / max|ref| <= 4e-3 per bf16 tensor.  Small cases element by element, the
+full-size workload on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import linear as ol
+from oracle import numerics
+from synth import configs
+from tests.gpu_util import dev_bf16, dev_u8, host_bits, host_f64, say
+
+import sharded_linear_amd as sl
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 4e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    yield
+    torch.cuda.synchronize()
+
+
+def _want_bits(packed, scales):
+    """bf16 patterns of the oracle's unscaled decode (exact products, so the conversion is too)."""
+    return synth.f32_to_bf16_bits(numerics.nvfp4_dequant(packed, scales, 1.0).astype(np.float32))
+
+
+def test_materialize_every_code_with_every_scale():
+    """Each of the 16 codes under each of the 254 finite scale bytes, in both nibble positions."""
+    say("case materialise: every code x every finite scale")
+    sc = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    rows = sc.size
+    lo = np.arange(16, dtype=np.uint8)
+    row = np.concatenate([lo[0::2] | (lo[1::2] << 4), lo[::-1][0::2] | (lo[::-1][1::2] << 4)])   # 32 codes
+    packed = np.tile(row, (rows, 1))
+    scales = np.stack([sc, sc[::-1]], axis=1)
+    Wm = sl.sl_nvfp4_materialize(dev_u8(packed), dev_u8(scales))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(Wm), _want_bits(packed, scales))
+
+
+def test_materialize_nan_scale():
+    say("case materialise: NaN scale bytes")
+    packed = np.full((2, 8), 0x52, np.uint8)
+    scales = np.array([[0x7F], [0xFF]], np.uint8)
+    Wm = sl.sl_nvfp4_materialize(dev_u8(packed), dev_u8(scales))
+    torch.cuda.synchronize()
+    assert torch.isnan(Wm.float()).all()
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (7, 48), (300, 1040), (4097, 272)])
+def test_materialize_random_bytes(rows, cols):
+    say(f"case materialise rows={rows} cols={cols}")
+    rng = np.random.default_rng(rows * 3 + cols)
+    packed = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (rows, cols // 16), dtype=np.uint8) | (rng.integers(0, 2, (rows, cols // 16),
+                                                                                          dtype=np.uint8) << 7)
+    Wm = sl.sl_nvfp4_materialize(dev_u8(packed), dev_u8(scales))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(Wm), _want_bits(packed, scales))
+
+
+def _nvfp4_case(T, n_in, n_out, seed):
+    q, s, t = synth.nvfp4_normal((n_out, n_in), seed * 10, synth.W_STD)
+    X = synth.normal_bf16((T, n_in), seed * 10 + 1)
+    dY = synth.normal_bf16((T, n_out), seed * 10 + 2)
+    return q, s, t, X, dY
+
+
+def _run(q, s, t, X, dY):
+    Wm = sl.sl_nvfp4_materialize(dev_u8(q), dev_u8(s))
+    Y = sl.sl_linear_fwd_nvfp4w(dev_bf16(X), Wm, t)
+    dX = sl.sl_linear_dgrad_nvfp4w(dev_bf16(dY), Wm, t)
+    torch.cuda.synchronize()
+    return Y, dX
+
+
+@pytest.mark.parametrize("T,n_in,n_out", [(1, 16, 8), (7, 48, 40), (300, 272, 520), (513, 1040, 776),
+                                          (1000, 2064, 264), (3333, 3344, 4104)])
+def test_fwd_dgrad_elementwise(T, n_in, n_out):
+    say(f"case nvfp4w T={T} in={n_in} out={n_out}")
+    q, s, t, X, dY = _nvfp4_case(T, n_in, n_out, T + n_in)
+    Y, dX = _run(q, s, t, X, dY)
+    e_y = ol.rel_err(host_f64(Y), ol.linear_fwd_nvfp4w(X, q, s, t))
+    e_dx = ol.rel_err(host_f64(dX), ol.linear_dgrad_nvfp4w(dY, q, s, t))
+    say(f"  rel err Y {e_y:.2e} dX {e_dx:.2e} (tensor scale {t:.3e})")
+    assert e_y <= TOL_BF16 and e_dx <= TOL_BF16
+
+
+@pytest.mark.parametrize("cfg", range(21))
+def test_tensor_scale_in_every_tile_config(monkeypatch, cfg):
+    """The tensor scale is applied in each configuration's epilogue (forced via SL_GEMM_CONFIG)."""
+    T, n_in, n_out = 1000, 2064, 520
+    say(f"case nvfp4w cfg={cfg} T={T} in={n_in} out={n_out}")
+    monkeypatch.setenv("SL_GEMM_CONFIG", str(cfg))
+    q, s, t, X, dY = _nvfp4_case(T, n_in, n_out, 77 + cfg)
+    Y, dX = _run(q, s, t, X, dY)
+    e_y = ol.rel_err(host_f64(Y), ol.linear_fwd_nvfp4w(X, q, s, t))
+    e_dx = ol.rel_err(host_f64(dX), ol.linear_dgrad_nvfp4w(dY, q, s, t))
+    say(f"  rel err Y {e_y:.2e} dX {e_dx:.2e}")
+    assert e_y <= TOL_BF16 and e_dx <= TOL_BF16
+
+
+def test_unit_tensor_scale_matches_bf16_entry_points():
+    """With t = 1 the scaled products are the plain bf16 products over the materialised weight,
+    bit for bit (multiplying the accumulators by 1 changes nothing)."""
+    say("case nvfp4w t=1 against sl_linear_fwd / sl_linear_dgrad")
+    q, s, _, X, dY = _nvfp4_case(520, 1040, 776, 5)
+    Wm = sl.sl_nvfp4_materialize(dev_u8(q), dev_u8(s))
+    Xd, dYd = dev_bf16(X), dev_bf16(dY)
+    a, b = sl.sl_linear_fwd_nvfp4w(Xd, Wm, 1.0), sl.sl_linear_fwd(Xd, Wm)
+    c, d = sl.sl_linear_dgrad_nvfp4w(dYd, Wm, 1.0), sl.sl_linear_dgrad(dYd, Wm)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(c.view(torch.int16), d.view(torch.int16))
+
+
+def test_full_size_workload_sampled():
+    """The NVFP4-weight MLP workload at full size: the whole materialised weight bit for bit, Y and
+    dX on sampled rows the oracle computes one by one."""
+    w = configs.WORKLOADS["c7"]
+    rng = np.random.default_rng(7)
+    for name in w.step_params:
+        o, i = w.params[name]
+        say(f"  c7 {name} [{o},{i}]")
+        q, s, t = configs.weight(w, name)
+        Wm = sl.sl_nvfp4_materialize(dev_u8(q), dev_u8(s))
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(Wm), _want_bits(q, s))
+        X, dY = configs.x(w, name, 0), configs.dy(w, name, 0)
+        Y = sl.sl_linear_fwd_nvfp4w(dev_bf16(X), Wm, t)
+        dX = sl.sl_linear_dgrad_nvfp4w(dev_bf16(dY), Wm, t)
+        torch.cuda.synchronize()
+        rows = np.sort(rng.choice(w.tokens, 48, replace=False))
+        e_y = ol.rel_err(host_f64(Y)[rows], ol.linear_fwd_nvfp4w(X[rows], q, s, t))
+        e_dx = ol.rel_err(host_f64(dX)[rows], ol.linear_dgrad_nvfp4w(dY[rows], q, s, t))
+        say(f"  c7 {name} sampled rel err Y {e_y:.2e} dX {e_dx:.2e}")
+        assert e_y <= TOL_BF16 and e_dx <= TOL_BF16
