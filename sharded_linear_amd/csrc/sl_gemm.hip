@@ -452,14 +452,14 @@ Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a
   int cfg = config_override(kind);
   if (cfg < 0) {
     cfg = kind == Kind::Wgrad ? 10 : pick_config(M, N);
-    // 256x256 tiles: the fixed-order kernels measured ahead of the compiler-scheduled one.  The
-    // weight gradient (both operands MN-major, whole cache lines per 32-k row) takes 4 waves with
-    // a 4-stage ring of 32 k; forward products take 8 waves with 2 stages of 64 k (a 32-k row of
-    // a K-major operand is half a cache line); dgrad, with one operand of each kind, the first
-    // for long K and the second otherwise.
-    if (cfg == 10) cfg = kind == Kind::Wgrad ? 15 : kind == Kind::Fwd ? 17 : (K >= 6144 ? 15 : 17);
+    // 256x256 tiles: the fixed-order 8-wave kernel on the 16x16x32 instruction (2 stages of 64 k)
+    // for all three products.  Against the 32x32x16 kernels (fwd: 8 waves, 2 x 64 k; dgrad and
+    // wgrad: 4 waves, 4 x 32 k) it measured 2-9 % ahead on the forward and up to 18 % on the
+    // weight gradients of short-K shapes: the part holds a higher clock under the 16x16 form.
+    if (cfg == 10) cfg = 21;
     // 256x128 tiles (shapes whose 256x256 tile count leaves CUs idle): the fixed-order 4-wave
     // kernel with a 3-stage ring of 64 k, measured 20 % ahead of the compiler-scheduled one on dgrad
+    // (its 16x16x32 twin, cfg 23, measured 5 % behind it there)
     if (cfg == 3 && kind != Kind::Wgrad) cfg = 19;
   }
   Plan p = make_plan_cfg(kind, mxfp8, M, N, K, a_bytes, b_bytes, cfg);

@@ -28,7 +28,7 @@ namespace sl2 {
 
 
 // ---- K-major operand: LDS [R rows][BK] bf16 -----------------------------------------------
-template <int R, int BK>
+template <int R, int BK, int SW = 0>
 struct KMaj {
   static constexpr int kRowBytes = BK * 2;
   static constexpr int kCPR = BK / 8;                  // 16-byte chunks per row
@@ -39,9 +39,20 @@ struct KMaj {
   // fragment (32 rows, two chunks) runs at the rate of linear addresses -- full LDS rate with 8
   // waves per CU -- with these, while the 64-byte-row alternative ((r >> 1) ^ (r >> 3)) & 3,
   // conflict-free on paper for 8 and 16 consecutive lanes, ran 1.7x slower.
+  // SW 1 serves the 16x16x32 fragment read (16 rows, four chunks) at BK 64: a ds_read_b128 pairs
+  // lanes 0-7 with 16-23 (rows r with chunks c, c+1), so the four same-parity rows of an 8-row
+  // block need distinct swizzles in bits {1,2} and in bits {0,2}, and rows r, r+8 distinct ones;
+  // {0,3,5,6} by bits 1-2 of r, complemented for rows 8-15, meets all three and measured at the
+  // linear rate.
   __device__ static __forceinline__ int swz(int r) {
-    if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);
-    else return (r ^ (r >> 2)) & 3;
+    if constexpr (SW == 1) {
+      static_assert(BK == 64, "16x16 swizzle is defined for BK 64");
+      return ((0x6530 >> (4 * ((r >> 1) & 3))) & 7) ^ (((r >> 3) & 1) * 7);
+    } else if constexpr (BK == 64) {
+      return (r & 7) ^ ((r >> 3) & 1);
+    } else {
+      return (r ^ (r >> 2)) & 3;
+    }
   }
 
   // Wave `w` issues loads wl = w, w + waves, ...; lane i fills LDS bytes [1024 wl + 16 i, +16).
@@ -80,7 +91,7 @@ struct KMaj {
 };
 
 // ---- MN-major operand: LDS [BK rows (k)][R] bf16 -------------------------------------------
-template <int R, int BK>
+template <int R, int BK, int SW = 0>
 struct MNMaj {
   static constexpr int kRowBytes = R * 2;
   static constexpr int kCPR = R / 8;
@@ -90,7 +101,14 @@ struct MNMaj {
   // XOR swizzle of 16-byte chunks by k row: for the 4 rows x 16 free indices read by each
   // 16-lane group of ds_read_b64_tr_b16 (and the 4 x 32 read by 32 lanes), the 32-byte chunk
   // pairs are pair ^ {0, 5, 2, 7}, distinct within 128- and 256-byte bank windows.
-  __device__ static __forceinline__ int swz(int k) { return ((k & 3) ^ ((k & 1) << 2)) << 1; }
+  // SW 1 serves the 16x16x32 fragment read, whose 32 lanes read k rows kb..kb+3 and kb+8..kb+11
+  // of the same 16 free indices: those rows also flip the low pair bit ({1, 4, 3, 6}), so the
+  // eight 32-byte pieces fill a 256-byte window.  Bit 3 of k is constant over a fragment's rows,
+  // so its k32 steps and second read stay immediates.
+  __device__ static __forceinline__ int swz(int k) {
+    if constexpr (SW == 1) return (((k & 3) ^ ((k & 1) << 2)) ^ ((k >> 3) & 1)) << 1;
+    else return ((k & 3) ^ ((k & 1) << 2)) << 1;
+  }
 
   template <int WAVES, int LO = 0, int HI = kLoads / WAVES>
   __device__ static __forceinline__ void load(i32x4 rs, char* lds, int lane, int wave,
@@ -133,10 +151,10 @@ struct MNMaj {
   }
 };
 
-template <bool KM, int R, int BK>
-struct OpSel { using T = KMaj<R, BK>; };
-template <int R, int BK>
-struct OpSel<false, R, BK> { using T = MNMaj<R, BK>; };
+template <bool KM, int R, int BK, int SW = 0>
+struct OpSel { using T = KMaj<R, BK, SW>; };
+template <int R, int BK, int SW>
+struct OpSel<false, R, BK, SW> { using T = MNMaj<R, BK, SW>; };
 
 // Workgroup -> macro-tile: blocks are dealt round-robin to the XCDs, so the block id is first
 // remapped to make each XCD's blocks a contiguous run of tile ids; tile ids then walk groups of
@@ -252,6 +270,82 @@ __device__ __forceinline__ void store_tile(const Gemm2Args& g, f32x16 (&acc)[TM]
         if (m < g.M && n < g.N) {
           if (direct) {
             const float4 o = old[i % NB][t];
+            x = make_float4(o.x + x.x, o.y + x.y, o.z + x.z, o.w + x.w);
+          }
+          *reinterpret_cast<float4*>(C + int64_t(m) * ldc + n) = x;
+        }
+      }
+    }
+  }
+}
+
+// The same epilogue for 16x16 accumulator blocks (v_mfma_f32_16x16x32_bf16, again with the B
+// fragment first): lane l holds row 16 i + l%16 of the wave tile and, in its four registers, the
+// four consecutive columns 16 j + 4(l/16) + 0..3.  bf16 tiles are staged whole; fp32 tiles go
+// through the same 32-row rounds as above, two 16-row blocks per round.
+template <int WM, int WN, int TM, int TN, bool ACC>
+__device__ __forceinline__ void store_tile16(const Gemm2Args& g, f32x4v (&acc)[TM][TN], char* smem, int mw, int nw,
+                                             int split, int lane, int wave) {
+  using E = EpiOf<WM, WN, ACC>;
+  char* ep = smem + wave * E::kBytes;
+  const int rl = lane & 15, gl = lane >> 4;
+  const int rr = lane / E::kCPR, cr = lane % E::kCPR;
+  const int n = nw + cr * (16 / E::kES);
+  if constexpr (!ACC) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(acc[i][j][e] * g.alpha);
+        *reinterpret_cast<bf16x4*>(ep + E::off(i * 16 + rl, 2 * j + (gl >> 1)) + 8 * (gl & 1)) = v;
+      }
+    __bf16* C = static_cast<__bf16*>(g.c);
+#pragma unroll
+    for (int t = 0; t < WM / E::kRPI; ++t) {
+      const int r = t * E::kRPI + rr, m = mw + r;
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + E::off(r, cr));
+      if (m < g.M && n < g.N) *reinterpret_cast<uint4*>(C + int64_t(m) * g.ldc + n) = v;
+    }
+  } else {
+    static_assert(TM % 2 == 0, "two 16-row blocks per round");
+    constexpr int RI = 32 / E::kRPI;
+    const bool direct = g.splits == 1;
+    float* C = direct ? static_cast<float*>(g.c) : g.ws + int64_t(split) * g.M * g.N;
+    const int64_t ldc = direct ? g.ldc : g.N;
+    constexpr int NB = RI <= 8 ? 2 : 1;
+    float4 old[NB][RI];
+    auto load_old = [&](int h, float4 (&o)[RI]) {
+#pragma unroll
+      for (int t = 0; t < RI; ++t) {
+        const int m = mw + h * 32 + t * E::kRPI + rr;
+        o[t] = (m < g.M && n < g.N) ? *reinterpret_cast<const float4*>(C + int64_t(m) * ldc + n)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    if (direct && NB == 2) load_old(0, old[0]);
+#pragma unroll
+    for (int h = 0; h < TM / 2; ++h) {
+      if constexpr (NB == 2) {
+        if (direct && h + 1 < TM / 2) load_old(h + 1, old[(h + 1) & 1]);
+      } else {
+        if (direct) load_old(h, old[0]);
+      }
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const f32x4v a = acc[2 * h + ii][j];
+          *reinterpret_cast<float4*>(ep + E::off(ii * 16 + rl, 4 * j + gl)) = make_float4(a[0], a[1], a[2], a[3]);
+        }
+#pragma unroll
+      for (int t = 0; t < RI; ++t) {
+        const int r = t * E::kRPI + rr, m = mw + h * 32 + r;
+        float4 x = *reinterpret_cast<const float4*>(ep + E::off(r, cr));
+        if (m < g.M && n < g.N) {
+          if (direct) {
+            const float4 o = old[h % NB][t];
             x = make_float4(o.x + x.x, o.y + x.y, o.z + x.z, o.w + x.w);
           }
           *reinterpret_cast<float4*>(C + int64_t(m) * ldc + n) = x;
@@ -392,12 +486,17 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
 // Barrier B(s+1), between the steps of stage s, certifies (i) every wave's loads of stage s + 1
 // have landed (each wave waits for its own with vmcnt first) and (ii) every wave has read all of
 // stage s (its second-step fragments were waited for), so its slot can take stage s + S.
-template <bool A_KM, bool B_KM, bool ACC, int S, int WGM, int WGN, int BK_, int BN_ = 256>
+//
+// MF selects the matrix instruction: 32 for v_mfma_f32_32x32x16_bf16 (k16 steps, 32x32 blocks),
+// 16 for v_mfma_f32_16x16x32_bf16 (k32 steps, 16x16 blocks).  Both run at the same rate per clock,
+// but the 16x16 form draws less power, so the part holds a higher clock under it.
+template <bool A_KM, bool B_KM, bool ACC, int S, int WGM, int WGN, int BK_, int BN_ = 256, int MF = 32>
 struct G4 {
   static constexpr int BM = 256, BN = BN_, BK = BK_, WAVES = WGM * WGN, WM = BM / WGM, WN = BN / WGN;
-  static constexpr int TM = WM / 32, TN = WN / 32;
-  using OA = typename OpSel<A_KM, BM, BK>::T;
-  using OB = typename OpSel<B_KM, BN, BK>::T;
+  static constexpr int TM = WM / MF, TN = WN / MF;
+  static constexpr int KS = 512 / MF;                   // k per MFMA step
+  using OA = typename OpSel<A_KM, BM, BK, MF == 16 ? 1 : 0>::T;
+  using OB = typename OpSel<B_KM, BN, BK, MF == 16 ? 1 : 0>::T;
   static constexpr int kStage = OA::kBytes + OB::kBytes;
   static constexpr int LA = OA::kLoads / WAVES, LB = OB::kLoads / WAVES, LPS = LA + LB;
   static constexpr int kRing = S * kStage;
@@ -426,6 +525,23 @@ __device__ __forceinline__ uint32_t mnmaj_frag_off(int f0, int lane) {
   return uint32_t(k * O::kRowBytes + (((f >> 3) ^ O::swz(k)) << 4) + ((f & 7) << 1));
 }
 
+// The 16x16x32 forms: a fragment is 16 rows (or free indices) x 32 k, lane l holding row l%16
+// and k 8(l/16) .. 8(l/16)+7.  K-major: the swizzle repeats every 16 rows, so fragments add
+// immediates and each k32 step has its own offset.  MN-major: the four 16-lane groups read k
+// rows 8g .. 8g+3 (and 8g+4 .. 8g+7 in the second read) of the same 16 free indices.
+template <class O>
+__device__ __forceinline__ uint32_t kmaj_frag_off16(int r0, int ks, int lane) {
+  const int r = r0 + (lane & 15), c = ks * 4 + (lane >> 4);
+  return uint32_t(r * O::kRowBytes + ((c ^ O::swz(r)) << 4));
+}
+template <class O>
+__device__ __forceinline__ uint32_t mnmaj_frag_off16(int f0, int lane) {
+  const int g = lane >> 4, s = lane & 15, j = s >> 2, q = s & 3;
+  const int f = f0 + 4 * q;
+  const int k = 8 * g + j;
+  return uint32_t(k * O::kRowBytes + (((f >> 3) ^ O::swz(k)) << 4) + ((f & 7) << 1));
+}
+
 template <int OFF>
 __device__ __forceinline__ bf16x8 lds_rd128(uint32_t addr) {
   const auto* p = reinterpret_cast<const __attribute__((address_space(3))) uint4*>(addr + OFF);
@@ -443,9 +559,12 @@ __device__ __forceinline__ bf16x8 lds_rd_tr(uint32_t addr) {
 template <int N>
 __device__ __forceinline__ void asm_wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" : : "i"(N) : "memory"); }
 
-template <bool A_KM, bool B_KM, bool ACC, int S, int WGM, int WGN, int BK_, int BN_>
+template <bool A_KM, bool B_KM, bool ACC, int S, int WGM, int WGN, int BK_, int BN_, int MF>
 __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
-  using P = G4<A_KM, B_KM, ACC, S, WGM, WGN, BK_, BN_>;
+  using P = G4<A_KM, B_KM, ACC, S, WGM, WGN, BK_, BN_, MF>;
+  constexpr int KS = P::KS;
+  using AccT = std::conditional_t<MF == 32, f32x16, f32x4v>;
+  constexpr int NACC = MF == 32 ? 16 : 4;
   using OA = typename P::OA;
   using OB = typename P::OB;
   constexpr int BK = P::BK, WAVES = P::WAVES, WM = P::WM, WN = P::WN, TM = P::TM, TN = P::TN;
@@ -487,41 +606,45 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
   const uint32_t kb_step = B_KM ? BK * 2 : uint32_t(BK * g.ldb * 2);
   const uint32_t lds0 = lds_addr(smem);
 
-  // fragment read offsets (per lane), K-major: one per k16 step; MN-major: one per fragment
-  constexpr int NPS = BK / 16;
+  // fragment read offsets (per lane), K-major: one per MFMA step; MN-major: one per fragment
+  constexpr int NPS = BK / KS;
   uint32_t ofa[A_KM ? NPS : TM], ofb[B_KM ? NPS : TN];
+  auto kfo_a = [&](int ks) { return MF == 32 ? kmaj_frag_off<OA>(wm * WM, ks, lane) : kmaj_frag_off16<OA>(wm * WM, ks, lane); };
+  auto kfo_b = [&](int ks) { return MF == 32 ? kmaj_frag_off<OB>(wn * WN, ks, lane) : kmaj_frag_off16<OB>(wn * WN, ks, lane); };
+  auto mfo_a = [&](int f0) { return MF == 32 ? mnmaj_frag_off<OA>(f0, lane) : mnmaj_frag_off16<OA>(f0, lane); };
+  auto mfo_b = [&](int f0) { return MF == 32 ? mnmaj_frag_off<OB>(f0, lane) : mnmaj_frag_off16<OB>(f0, lane); };
   if constexpr (A_KM)
 #pragma unroll
-    for (int ks = 0; ks < NPS; ++ks) ofa[ks] = kmaj_frag_off<OA>(wm * WM, ks, lane);
+    for (int ks = 0; ks < NPS; ++ks) ofa[ks] = kfo_a(ks);
   else
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ofa[i] = mnmaj_frag_off<OA>(wm * WM + 32 * i, lane);
+    for (int i = 0; i < TM; ++i) ofa[i] = mfo_a(wm * WM + MF * i);
   if constexpr (B_KM)
 #pragma unroll
-    for (int ks = 0; ks < NPS; ++ks) ofb[ks] = OA::kBytes + kmaj_frag_off<OB>(wn * WN, ks, lane);
+    for (int ks = 0; ks < NPS; ++ks) ofb[ks] = OA::kBytes + kfo_b(ks);
   else
 #pragma unroll
-    for (int j = 0; j < TN; ++j) ofb[j] = OA::kBytes + mnmaj_frag_off<OB>(wn * WN + 32 * j, lane);
+    for (int j = 0; j < TN; ++j) ofb[j] = OA::kBytes + mfo_b(wn * WN + MF * j);
 
-  f32x16 acc[TM][TN];
+  AccT acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < NACC; ++r) acc[i][j][r] = 0.f;
   bf16x8 fa[2][TM], fb[2][TN];
 
-  // fragment i (A) or j (B) of k16 step ks from the stage at LDS byte `base`
+  // fragment i (A) or j (B) of MFMA step ks from the stage at LDS byte `base`
   auto read_a = [&](bf16x8& d, uint32_t base, auto ic_i, auto ic_ks) {
     constexpr int i = decltype(ic_i)::value, ks = decltype(ic_ks)::value;
-    if constexpr (A_KM) d = lds_rd128<i * 32 * OA::kRowBytes>(base + ofa[ks]);
-    else d = lds_rd_tr<ks * 16 * OA::kRowBytes, (ks * 16 + 4) * OA::kRowBytes>(base + ofa[i]);
+    if constexpr (A_KM) d = lds_rd128<i * MF * OA::kRowBytes>(base + ofa[ks]);
+    else d = lds_rd_tr<ks * KS * OA::kRowBytes, (ks * KS + 4) * OA::kRowBytes>(base + ofa[i]);
   };
   auto read_b = [&](bf16x8& d, uint32_t base, auto ic_j, auto ic_ks) {
     constexpr int j = decltype(ic_j)::value, ks = decltype(ic_ks)::value;
-    if constexpr (B_KM) d = lds_rd128<j * 32 * OB::kRowBytes>(base + ofb[ks]);
-    else d = lds_rd_tr<ks * 16 * OB::kRowBytes, (ks * 16 + 4) * OB::kRowBytes>(base + ofb[j]);
+    if constexpr (B_KM) d = lds_rd128<j * MF * OB::kRowBytes>(base + ofb[ks]);
+    else d = lds_rd_tr<ks * KS * OB::kRowBytes, (ks * KS + 4) * OB::kRowBytes>(base + ofb[j]);
   };
   // wave-load `l` (A: l < LA, then B) of the stage at k tile kt into LDS slot `slot`
   auto load_one = [&](auto ic_l, int kt, int slot, bool ragged) {
@@ -535,7 +658,11 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
     }
   };
   // Memory operation m of a step: m < NR reads fragment piece m into buffer NX; after that the
-  // loads [L0, L0 + LPS/2) of stage kt into slot `slot` (when `loads`).
+  // loads [L0, L0 + LPS/2) (or all LPS when ONE) of stage kt into slot `slot` (when `loads`).
+  // ONE (the 16x16 kernels): a stage's loads all go out in the step right after the barrier that
+  // frees its slot.  Under the 16x16 instruction the part clocks higher, a stage takes less time,
+  // and loads issued a step later than that no longer land before the barrier that waits for them.
+  constexpr bool ONE = MF == 16;
   constexpr int NR = TM + TN, LH = LPS / 2;
   static_assert(LPS % 2 == 0, "loads split over two steps");
   auto memop = [&](auto ic_m, auto ic_nx, auto ic_ks, auto ic_l0, uint32_t rbase, bool loads, int kt, int slot,
@@ -548,32 +675,44 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
       if (loads) load_one(ic<l0 + m - NR>{}, kt, slot, ragged);
     }
   };
-  // One k16 step: TM x TN MFMAs on buffer CUR; NM memory operations spread over them.
+  // One MFMA step: TM x TN MFMAs on buffer CUR with NM memory operations among them.  The
+  // fragment reads go out over the first three quarters of the MFMAs, so they have landed when
+  // the step ends (the stage barrier waits for them); the loads are spread evenly over the whole
+  // step, one every NQ/NL MFMAs, which keeps the texture-address queue from filling.
   auto step = [&](auto ic_cur, auto ic_nm, auto&& mem) {
     constexpr int cur = decltype(ic_cur)::value, NM = decltype(ic_nm)::value;
     static_for<TM * TN>([&](auto qc) {
       constexpr int q = decltype(qc)::value, i = q / TN, j = q % TN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
-      constexpr int lo = q * NM / (TM * TN), hi = (q + 1) * NM / (TM * TN);
-      static_for<hi - lo>([&](auto mc) { mem(ic<lo + decltype(mc)::value>{}); });
+      if constexpr (MF == 32)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+      constexpr int NQ = TM * TN, NRD = NR < NM ? NR : NM, NL = NM - NRD;
+      constexpr int RQ = NQ * 3 / 4 > 0 ? NQ * 3 / 4 : 1;
+      constexpr int rlo = q < RQ ? q * NRD / RQ : NRD, rhi = q < RQ ? (q + 1) * NRD / RQ : NRD;
+      static_for<rhi - rlo>([&](auto mc) { mem(ic<rlo + decltype(mc)::value>{}); });
+      constexpr int llo = NL ? (2 * q * NL + NQ) / (2 * NQ) : 0, lhi = NL ? (2 * (q + 1) * NL + NQ) / (2 * NQ) : 0;
+      static_for<lhi - llo>([&](auto mc) { mem(ic<NRD + llo + decltype(mc)::value>{}); });
       __builtin_amdgcn_sched_barrier(0);
     });
   };
 
   {
-    // Prologue: stages 0..S-2 and the first half of stage S-1 (the host launches this kernel only
-    // when every split has at least S stages).  From then on the loads of stage x are issued in two
-    // halves: the first in the second step of stage x - S (just after the barrier that frees its
-    // slot), the second in the first step of stage x - S + 1, which spreads them over the MFMAs.
+    // Prologue: stages 0..S-2 and the first half of stage S-1, or all S stages when ONE (the host
+    // launches this kernel only when every split has at least S stages).  From then on the loads of
+    // stage x are issued in the last step of stage x - S (just after the barrier that frees its
+    // slot): all of them when ONE, else the first half there and the second in the first step of
+    // stage x - S + 1.  Either way, at barrier B(s+1) the loads issued after stage s + 1's are the
+    // S - 2 whole stages s + 2 .. s + S - 1.
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const bool rag = kt0 + s == nkt - 1;
-      if (s < S - 1) static_for<LPS>([&](auto lc) { load_one(lc, kt0 + s, s, rag); });
+      if (ONE || s < S - 1) static_for<LPS>([&](auto lc) { load_one(lc, kt0 + s, s, rag); });
       else static_for<LH>([&](auto lc) { load_one(lc, kt0 + s, s, rag); });
     }
-    // stage 0 is complete once at most the S-2 later stages' loads (the last one only half issued)
-    // are outstanding
-    asm_wait_vm<LPS * (S - 2) + LH>();
+    // stage 0 is complete once at most the later prologue stages' loads (S - 1 of them, the last
+    // one only half issued unless ONE) are outstanding
+    asm_wait_vm<ONE ? LPS * (S - 1) : LPS * (S - 2) + LH>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     static_for<TM>([&](auto ic_i) { read_a(fa[0][decltype(ic_i)::value], lds0, ic_i, ic<0>{}); });
@@ -585,7 +724,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
     // (NPS is even), reading the next stage's step 0 into buffer 0 and issuing the first half of
     // stage s + S into s's slot.  At the barrier the loads issued after the last one of stage
     // s + 1 are the S - 2 whole stages s + 2 .. s + S - 1.
-    constexpr int NPS_ = BK / 16;
+    constexpr int NPS_ = BK / KS;
     static_assert(NPS_ % 2 == 0, "steps per stage");
     auto stage = [&](int s, auto ic_vm, auto ic_la, auto ic_lb, auto ic_last) {
       constexpr int VM = decltype(ic_vm)::value;
@@ -594,7 +733,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
       const uint32_t cur = lds0 + slot * kStage;
       static_for<NPS_ - 1>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
-        constexpr bool ld = LDA && t == 0;
+        constexpr bool ld = !ONE && LDA && t == 0;
         const int kt = kt0 + s + S - 1, lslot = (s + S - 1) % S;
         const bool rag = kt == nkt - 1;
         step(ic<t % 2>{}, ic<ld ? NR + LH : NR>{},
@@ -608,7 +747,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
         const uint32_t nxt = lds0 + ((s + 1) % S) * kStage;
         const int kt = kt0 + s + S;
         const bool rag = kt == nkt - 1;
-        step(ic<1>{}, ic<LDB ? NR + LH : NR>{},
+        step(ic<1>{}, ic<LDB ? NR + (ONE ? LPS : LH) : NR>{},
              [&](auto ic_m) { memop(ic_m, ic<0>{}, ic<0>{}, ic<0>{}, nxt, LDB, kt, slot, rag); });
       } else {
         step(ic<1>{}, ic<0>{}, [&](auto) {});
@@ -627,7 +766,8 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
   }
   asm_wait_vm<0>();
   __syncthreads();    // every wave is past its last operand read: the ring becomes epilogue space
-  store_tile<WM, WN, TM, TN, ACC>(g, acc, smem, m0 + wm * WM, n0 + wn * WN, split, lane, wave);
+  if constexpr (MF == 32) store_tile<WM, WN, TM, TN, ACC>(g, acc, smem, m0 + wm * WM, n0 + wn * WN, split, lane, wave);
+  else store_tile16<WM, WN, TM, TN, ACC>(g, acc, smem, m0 + wm * WM, n0 + wn * WN, split, lane, wave);
 }
 
 template <int BM, int BN, int BK, int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int SCHED = 0, int OCC = 1>
@@ -650,10 +790,10 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-template <int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int BK = 32, int BN = 256>
+template <int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int BK = 32, int BN = 256, int MF = 32>
 int launch_g4(hipStream_t st, Gemm2Args g) {
-  using P = G4<A_KM, B_KM, ACC, S, WGM, WGN, BK, BN>;
-  auto kfn = gemm4<A_KM, B_KM, ACC, S, WGM, WGN, BK, BN>;
+  using P = G4<A_KM, B_KM, ACC, S, WGM, WGN, BK, BN, MF>;
+  auto kfn = gemm4<A_KM, B_KM, ACC, S, WGM, WGN, BK, BN, MF>;
   static bool attr = false;
   if (!attr) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, P::kLds) != hipSuccess)
@@ -696,6 +836,7 @@ int launch_g4(hipStream_t st, Gemm2Args g) {
 //  18: 256x256, BK 64, 2 stages, 4 waves (128x128 wave tiles), fixed issue order        LDS 128 KiB
 //  19: 256x128, BK 64, 3 stages, 4 waves (128x64 wave tiles), fixed issue order         LDS 144 KiB
 //  20: 256x128, BK 32, 4 stages, 4 waves (128x64 wave tiles), fixed issue order         LDS  96 KiB
+//  21-23: as 17-19 with v_mfma_f32_16x16x32_bf16 (16x16 blocks, k32 steps)
 #define SL2_DISPATCH(AK, BKM, ACC)                                                                 \
   switch (g.cfg) {                                                                                 \
     case 0: return sl2::launch_cfg<256, 256, 32, 4, 2, 2, AK, BKM, ACC>(st, g);                   \
@@ -719,6 +860,9 @@ int launch_g4(hipStream_t st, Gemm2Args g) {
     case 18: return sl2::launch_g4<2, 2, 2, AK, BKM, ACC, 64>(st, g);                              \
     case 19: return sl2::launch_g4<3, 2, 2, AK, BKM, ACC, 64, 128>(st, g);                         \
     case 20: return sl2::launch_g4<4, 2, 2, AK, BKM, ACC, 32, 128>(st, g);                         \
+    case 21: return sl2::launch_g4<2, 2, 4, AK, BKM, ACC, 64, 256, 16>(st, g);                     \
+    case 22: return sl2::launch_g4<2, 2, 2, AK, BKM, ACC, 64, 256, 16>(st, g);                     \
+    case 23: return sl2::launch_g4<3, 2, 2, AK, BKM, ACC, 64, 128, 16>(st, g);                     \
     default: return -1;                                                                            \
   }
 
@@ -727,7 +871,8 @@ int gemm2_dgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, false, false) 
 int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) }
 
 int gemm2_min_stages(int cfg) {
-  return cfg == 15 || cfg == 16 || cfg == 20 ? 4 : cfg == 17 || cfg == 18 ? 2 : cfg == 19 ? 3 : 1;
+  return cfg == 15 || cfg == 16 || cfg == 20 ? 4 : cfg == 17 || cfg == 18 || cfg == 21 || cfg == 22 ? 2
+         : cfg == 19 || cfg == 23 ? 3 : 1;
 }
 
 void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
@@ -735,7 +880,8 @@ void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
   static const int t[kGemm2Configs][2] = {
       {256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256}, {256, 256},
       {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {128, 256},
-      {256, 128}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {256, 128}};
+      {256, 128}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {256, 128},
+      {256, 256}, {256, 256}, {256, 128}};
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }
