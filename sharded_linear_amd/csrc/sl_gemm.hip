@@ -457,6 +457,13 @@ Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a
     // wgrad: 4 waves, 4 x 32 k) it measured 2-9 % ahead on the forward and up to 18 % on the
     // weight gradients of short-K shapes: the part holds a higher clock under the 16x16 form.
     if (cfg == 10) cfg = 21;
+    // A weight gradient whose 256x256 tiles cover about half of the 256 CUs, but whose 256x128
+    // tiles make one full round, runs those unsplit on the 32x32x16 fixed-order kernel (cfg 20):
+    // 5 % ahead of two K splits plus the reduce (config 2 fc2).
+    if (kind == Kind::Wgrad && cfg == 21) {
+      const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256), t128 = ((M + 255) / 256) * ((N + 127) / 128);
+      if (t256 <= 144 && t128 >= 240 && t128 <= 288) cfg = 20;
+    }
     // 256x128 tiles (shapes whose 256x256 tile count leaves CUs idle): the fixed-order 4-wave
     // kernel with a 3-stage ring of 64 k, measured 20 % ahead of the compiler-scheduled one on dgrad
     // (its 16x16x32 twin, cfg 23, measured 5 % behind it there)
