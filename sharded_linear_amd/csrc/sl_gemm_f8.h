@@ -18,6 +18,7 @@ struct F8Args {
   int splits = 1;       // split-K (accumulating kernel): K stages of 128 per split
   int kt_per_split = 0;
   float* ws = nullptr;  // split-K partial planes [splits][M][N]
+  float alpha = 1.0f;   // bf16 results are alpha * (A . B^T)
 };
 
 // C = A.B^T (bf16 out) over block-scaled fp8 operands.

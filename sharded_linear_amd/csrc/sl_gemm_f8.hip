@@ -11,7 +11,10 @@
 //    row m in group g multiplies the 32-element block g of that row.  So each lane loads the two
 //    16-byte chunks 16g and 32+16g of the k step and the scale of block (k0/32 + g).
 //    Codes travel HBM->LDS directly (buffer_load ... lds, rows of 128 bytes, swizzled like the
-//    bf16 tiles); each stage also carries one dword of 4 block scales per row.
+//    bf16 tiles); each stage also carries one dword of 4 block scales per row.  In the
+//    fp32-accumulating form the MFMAs take the B fragment (with its scales) first, so the
+//    accumulators hold C^T blocks as in the bf16 kernels and the read-modify-write of main_grad
+//    goes through the same LDS-staged epilogue (16-byte row accesses).
 //  * dgrad / wgrad see the MXFP8 operand blocked along their N, not K; it is dequantised
 //    exactly into a bf16 workspace by mx_dequant_bf16 (an E4M3 value times a power of two has
 //    at most 4 significant bits) and the bf16 GEMM kernels run on it.
@@ -20,6 +23,7 @@
 #include <cstdint>
 
 #include "sl_device.h"
+#include "sl_epi.h"
 #include "sl_gemm_f8.h"
 
 namespace sl2 {
@@ -167,39 +171,24 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[i], fb[j], acc[i][j], 0, 0, 0, int((sca[i] >> sh) & 0xFFu), 0, int((scb[j] >> sh) & 0xFFu));
+          if constexpr (ACC)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fb[j], fa[i], acc[i][j], 0, 0, 0, int((scb[j] >> sh) & 0xFFu), 0, int((sca[i] >> sh) & 0xFFu));
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fa[i], fb[j], acc[i][j], 0, 0, 0, int((sca[i] >> sh) & 0xFFu), 0, int((scb[j] >> sh) & 0xFFu));
     }
   }
   wait_vmcnt<0>();
-
-  const int rib = 4 * (lane >> 5), cib = lane & 31;
   if constexpr (ACC) {
-    // fp32 result: lanes 0..31 of each row cover 32 consecutive columns (128 bytes).  Unsplit:
-    // the single read-modify-write of C; split: this split's partial into its own plane.
-    const bool direct = g.splits == 1;
-    float* C = direct ? static_cast<float*>(g.c) : g.ws + int64_t(split) * g.M * g.N;
-    const int64_t ldc = direct ? g.ldc : g.N;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WN + j * 32 + cib;
-        const int mb = m0 + wm * WM + i * 32 + rib;
-        float old[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mb + 8 * (r >> 2) + (r & 3);
-          old[r] = (direct && m < g.M && n < g.N) ? C[int64_t(m) * ldc + n] : 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mb + 8 * (r >> 2) + (r & 3);
-          if (m < g.M && n < g.N) C[int64_t(m) * ldc + n] = old[r] + acc[i][j][r];
-        }
-      }
+    __syncthreads();    // every wave is past its last operand read: the stage ring becomes epilogue space
+    store_tile<WM, WN, TM, TN, ACC>(g, acc, smem, m0 + wm * WM, n0 + wn * WN, split, lane, wave);
     return;
   }
+  // bf16 result (A fragment first: lane l holds column l%32 of each block, rows
+  // 8(r/4) + 4(l/32) + r%4): each store instruction covers 64 contiguous bytes of two rows, which
+  // measured ahead of staging the tile through LDS here.
+  const int rib = 4 * (lane >> 5), cib = lane & 31;
   const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
   __bf16* C = static_cast<__bf16*>(g.c);
 #pragma unroll
@@ -221,6 +210,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
       }
     }
 }
+
 
 // bf16 out[r][c] = E4M3(codes[r][c]) * 2^(scales[r][c/32] - 127), 16 elements per chunk and four
 // chunks per thread in flight (the kernel is bound by HBM bytes, 3 per element).  The product
@@ -270,8 +260,11 @@ __global__ void mx_dequant_bf16(const uint8_t* codes, const uint8_t* scales, uin
 
 template <int BM, int BN, int S, int WGM, int WGN, bool ACC = false>
 int launch_f8(hipStream_t st, F8Args g) {
-  constexpr int lds = S * (F8Tile<BM>::kBytes + F8Tile<BN>::kBytes +
-                           ((F8Tile<BM>::kScaleBytes + F8Tile<BN>::kScaleBytes + 255) / 256) * 256 + 256);
+  constexpr int ring = S * (F8Tile<BM>::kBytes + F8Tile<BN>::kBytes +
+                            ((F8Tile<BM>::kScaleBytes + F8Tile<BN>::kScaleBytes + 255) / 256) * 256 + 256);
+  constexpr int epi = WGM * WGN * EpiOf<BM / WGM, BN / WGN, ACC>::kBytes;
+  constexpr int lds = ring > epi ? ring : epi;
+  static_assert(lds <= 160 * 1024, "LDS");
   auto kfn = gemm_f8fwd<BM, BN, S, WGM, WGN, ACC>;
   static bool attr = false;
   if (!attr) {
