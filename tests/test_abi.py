@@ -77,6 +77,19 @@ def test_wgrad_validation():
     assert _lib.lib().sl_wgrad_workspace_bytes(0, 16, 16) == 0
 
 
+def test_wgrad_split_plan():
+    """The planner's split choices seen through the workspace query: a full chip of 256x256
+    tiles runs unsplit; half a chip of them with a full round of 256x128 tiles runs those unsplit;
+    fewer tiles split K (fp32 planes [splits][out][in])."""
+    ws = _lib.lib().sl_wgrad_workspace_bytes
+    assert ws(8192, 2048, 8192) == 0                   # 256 tiles of 256x256
+    assert ws(8192, 4096, 2048) == 0                   # 128 of 256x256, 256 of 256x128
+    assert ws(1000, 4000, 2050) == 0                   # 144 / 288, ragged
+    need = ws(8192, 2048, 1536)                        # 48 tiles: split
+    assert need > 0 and need % (1536 * 2048 * 4) == 0 and need // (1536 * 2048 * 4) >= 2
+    assert ws(8192, 1024, 2048) > 0                    # 32 tiles, 64 of 256x128: split
+
+
 def test_mxfp8_validation():
     L = _lib.lib()
     assert L.sl_linear_fwd_mxfp8(None, A, A, A, A, A, 16, 48, 16) == SL_ESHAPE     # in % 32
