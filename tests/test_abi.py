@@ -84,7 +84,7 @@ def test_wgrad_split_plan():
     ws = _lib.lib().sl_wgrad_workspace_bytes
     assert ws(8192, 2048, 8192) == 0                   # 256 tiles of 256x256
     assert ws(8192, 4096, 2048) == 0                   # 128 of 256x256, 256 of 256x128
-    assert ws(1000, 4000, 2050) == 0                   # 144 / 288, ragged
+    assert ws(1000, 4000, 2056) == 0                   # 144 / 288, ragged
     need = ws(8192, 2048, 1536)                        # 48 tiles: split
     assert need > 0 and need % (1536 * 2048 * 4) == 0 and need // (1536 * 2048 * 4) >= 2
     assert ws(8192, 1024, 2048) > 0                    # 32 tiles, 64 of 256x128: split

@@ -44,7 +44,7 @@ SMALL = [
     (1, 8, 8), (7, 24, 40), (128, 256, 512), (300, 264, 520), (513, 1032, 776),
     (4104, 264, 520), (1000, 2056, 264), (4100, 264, 3336), (3333, 3336, 4104),
     # weight gradient with 144 tiles of 256x256 and 288 of 256x128: the unsplit 256x128 rule, ragged
-    (1000, 4000, 2050),
+    (1000, 4000, 2056),
 ]
 
 
