@@ -140,6 +140,16 @@ int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, const uint8_t*
                                  const void* dY, float* main_grad, int64_t T, int64_t in,
                                  int64_t out, void* workspace, size_t workspace_bytes);
 
+/* sl_mxfp8_dequantize: out[r, c] (bf16) = deq(q, s)[r, c] = E4M3(q[r, c]) * 2^(s[r, c/32] - 127)
+ * for q[rows, cols] codes and s[rows, cols/32] scales (section 1.3 block of 32 above).  Exact under
+ * the representability rule above (results that are not normal bf16 values are unspecified).
+ * cols % 32 == 0 (SL_ESHAPE); q and out 16-byte aligned (SL_EALIGN); the caller owns all buffers.
+ * This is the expansion sl_linear_dgrad_mxfp8w and sl_linear_wgrad_accum_mxfp8x perform into
+ * their workspace; sl_linear_dgrad on its output gives the same dX bit for bit.
+ */
+int sl_mxfp8_dequantize(void* stream, const uint8_t* q, const uint8_t* s, void* out, int64_t rows,
+                        int64_t cols);
+
 /* ---------------------------------------------------------------------------------------------
  * All-MXFP8 step: the backward GEMMs in MXFP8 as well (NVIDIA Megatron-Core guide "Generalized
  * Tensor Parallelism", section 1.3: in the MXFP8 recipe each GEMM reads E4M3 elements with one

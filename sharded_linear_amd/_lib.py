@@ -40,6 +40,7 @@ PROTOTYPES = {
     "sl_mxfp8_wgrad_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64]),
     "sl_linear_wgrad_accum_mxfp8": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64,
                                                    c_vp, c_sz]),
+    "sl_mxfp8_dequantize": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64]),
     "sl_nvfp4_materialize": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64]),
     "sl_linear_fwd_nvfp4w": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_float, c_vp, c_i64, c_i64, c_i64]),
     "sl_linear_dgrad_nvfp4w": (ctypes.c_int, [c_vp, c_vp, c_vp, ctypes.c_float, c_vp, c_i64, c_i64, c_i64]),

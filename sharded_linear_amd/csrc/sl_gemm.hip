@@ -704,6 +704,17 @@ bool mx_bf16_path(int64_t rows, int64_t in, int64_t other_bytes) {
 
 }  // namespace
 
+extern "C" int sl_mxfp8_dequantize(void* stream, const uint8_t* q, const uint8_t* s, void* out, int64_t rows,
+                                   int64_t cols) {
+  if (rows < 0 || cols < 0) return SL_EINVAL;
+  if (cols % 32) return SL_ESHAPE;
+  if (rows >= kMaxExtent || cols >= kMaxExtent) return SL_ESHAPE;
+  if (rows == 0 || cols == 0) return SL_OK;
+  if (!q || !s || !out) return SL_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return SL_EALIGN;
+  return mx_dequant(static_cast<hipStream_t>(stream), q, s, out, rows, cols) == 0 ? SL_OK : SL_EHIP;
+}
+
 extern "C" size_t sl_mxfp8_workspace_bytes(int64_t T, int64_t in, int64_t out) {
   if (T <= 0 || in <= 0 || out <= 0 || in % 32) return 0;
   size_t need = 0;

@@ -172,6 +172,19 @@ def sl_linear_wgrad_accum_mxfp8x(Xq, Xs, dY, main_grad, workspace=None):
     return main_grad
 
 
+def sl_mxfp8_dequantize(q, s, out=None):
+    """bf16 out[r, c] = E4M3(q[r, c]) * 2^(s[r, c/32] - 127) for codes q[R, C] and scales s[R, C/32]."""
+    dev = _device(q)
+    R, C = q.shape
+    _want(q, "q", U8, (R, C), dev)
+    _want(s, "s", U8, (R, C // 32), dev)
+    if out is None:
+        out = torch.empty((R, C), dtype=BF16, device=dev)
+    _want(out, "out", BF16, (R, C), dev)
+    check("sl_mxfp8_dequantize", lib().sl_mxfp8_dequantize(_stream(dev), _ptr(q), _ptr(s), _ptr(out), R, C))
+    return out
+
+
 # ---- all-MXFP8 step ---------------------------------------------------------------------------
 
 def sl_mxfp8_quantize(x, rows=True, cols=True, out=None):

@@ -158,6 +158,17 @@ def test_nvfp4_validation():
         assert f(None, None, None, 1.0, None, 0, 64, 64) == SL_OK
 
 
+def test_mxfp8_dequantize_validation():
+    d = _lib.lib().sl_mxfp8_dequantize
+    assert d(None, A, A, A, 64, 48) == SL_ESHAPE                                  # cols % 32
+    assert d(None, A, A, A, -1, 64) == SL_EINVAL
+    assert d(None, None, A, A, 64, 64) == SL_EINVAL
+    assert d(None, A, None, A, 64, 64) == SL_EINVAL
+    assert d(None, MIS, A, A, 64, 64) == SL_EALIGN
+    assert d(None, A, A, MIS, 64, 64) == SL_EALIGN
+    assert d(None, None, None, None, 0, 64) == SL_OK
+
+
 def test_zero_fill_validation():
     L = _lib.lib()
     assert L.sl_grad_buffer_zero(None, A, -1) == SL_EINVAL

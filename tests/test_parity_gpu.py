@@ -12,6 +12,7 @@ import torch
 import synth
 from oracle import linear as ol
 from oracle import layout as olayout
+from oracle import numerics
 from synth import configs
 from tests.gpu_util import dev_bf16, dev_u8, host_bits, host_f64, say
 
@@ -341,6 +342,40 @@ def test_mxfp8_all_codes_decode_exactly(n_in):
         Y = host_f64(sl.sl_linear_fwd_mxfp8(dev_u8(Xq), dev_u8(Xs), dev_u8(Wq), dev_u8(Ws)))[0]
         want = ol.linear_fwd_mxfp8(Xq, Xs, Wq, Ws)[0]
         assert np.array_equal(Y, want), s
+
+
+@pytest.mark.parametrize("rows,cols", [(7, 32), (254, 256), (300, 1024)])
+def test_mxfp8_dequantize_bit_exact(rows, cols):
+    """sl_mxfp8_dequantize against the oracle's decode, bit for bit: every finite E4M3 code under
+    block scales from 2^-27 to 2^8 (all results normal bf16), ragged row counts."""
+    say(f"case mxfp8 dequantize rows={rows} cols={cols}")
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    rng = np.random.default_rng(rows + cols)
+    q = codes[rng.integers(0, codes.size, (rows, cols))]
+    q.reshape(-1)[: min(codes.size, q.size)] = codes[: min(codes.size, q.size)]
+    s = rng.integers(100, 136, (rows, cols // 32)).astype(np.uint8)
+    out = sl.sl_mxfp8_dequantize(dev_u8(q), dev_u8(s))
+    torch.cuda.synchronize()
+    want = synth.f32_to_bf16_bits(numerics.mxfp8_dequant(q, s).astype(np.float32))
+    assert np.array_equal(host_bits(out), want)
+
+
+def test_mxfp8_weight_expanded_once_matches_per_call_dgrad():
+    """A step that expands the MXFP8 weight once and runs the bf16 dgrad on it gives the per-call
+    entry point's dX bit for bit (the same exact expansion feeds the same GEMM)."""
+    T, n_in, n_out = 1000, 1024, 776
+    say(f"case mxfp8 weight expanded once T={T} in={n_in} out={n_out}")
+    Wq, Ws = synth.mxfp8_normal((n_out, n_in), 61, synth.W_STD)
+    dY = synth.normal_bf16((T, n_out), 62)
+    Wqd, Wsd, dYd = dev_u8(Wq), dev_u8(Ws), dev_bf16(dY)
+    Wd = sl.sl_mxfp8_dequantize(Wqd, Wsd)
+    a = sl.sl_linear_dgrad(dYd, Wd)
+    b = sl.sl_linear_dgrad_mxfp8w(dYd, Wqd, Wsd)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    e = ol.rel_err(host_f64(a), ol.linear_dgrad_mxfp8w(dY, Wq, Ws))
+    say(f"  rel err dX {e:.2e}")
+    assert e <= TOL_BF16
 
 
 def test_mxfp8_dequantised_operand_exact():
