@@ -464,10 +464,10 @@ Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a
       const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256), t128 = ((M + 255) / 256) * ((N + 127) / 128);
       if (t256 <= 144 && t128 >= 240 && t128 <= 288) cfg = 20;
     }
-    // 256x128 tiles (shapes whose 256x256 tile count leaves CUs idle): the fixed-order 4-wave
-    // kernel with a 3-stage ring of 64 k, measured 20 % ahead of the compiler-scheduled one on dgrad
-    // (its 16x16x32 twin, cfg 23, measured 5 % behind it there)
-    if (cfg == 3 && kind != Kind::Wgrad) cfg = 19;
+    // 256x128 tiles (shapes whose 256x256 tile count leaves CUs idle): the fixed-order 8-wave
+    // 16x16x32 kernel with a 3-stage ring of 64 k (64x64 wave tiles), measured 7 % ahead of the
+    // 4-wave 32x32x16 one (cfg 19) and 27 % ahead of the compiler-scheduled one on dgrad
+    if (cfg == 3 && kind != Kind::Wgrad) cfg = 24;
   }
   Plan p = make_plan_cfg(kind, mxfp8, M, N, K, a_bytes, b_bytes, cfg);
   // configurations that prefill a deep ring need that many k stages in every split

@@ -18,7 +18,7 @@ struct Gemm2Args {
   float alpha = 1.0f;   // bf16 results are alpha * (A . B^T), scaled in fp32 before rounding
 };
 
-constexpr int kGemm2Configs = 24;
+constexpr int kGemm2Configs = 25;
 
 // A K-major (k contiguous) and B K-major: forward.
 int gemm2_fwd(hipStream_t st, Gemm2Args g);

@@ -664,6 +664,7 @@ int launch_g4(hipStream_t st, Gemm2Args g) {
 //  19: 256x128, BK 64, 3 stages, 4 waves (128x64 wave tiles), fixed issue order         LDS 144 KiB
 //  20: 256x128, BK 32, 4 stages, 4 waves (128x64 wave tiles), fixed issue order         LDS  96 KiB
 //  21-23: as 17-19 with v_mfma_f32_16x16x32_bf16 (16x16 blocks, k32 steps)
+//  24: 256x128, BK 64, 3 stages, 8 waves 4x2 (64x64 wave tiles), fixed issue order, 16x16x32  LDS 144 KiB
 #define SL2_DISPATCH(AK, BKM, ACC)                                                                 \
   switch (g.cfg) {                                                                                 \
     case 0: return sl2::launch_cfg<256, 256, 32, 4, 2, 2, AK, BKM, ACC>(st, g);                   \
@@ -690,6 +691,7 @@ int launch_g4(hipStream_t st, Gemm2Args g) {
     case 21: return sl2::launch_g4<2, 2, 4, AK, BKM, ACC, 64, 256, 16>(st, g);                     \
     case 22: return sl2::launch_g4<2, 2, 2, AK, BKM, ACC, 64, 256, 16>(st, g);                     \
     case 23: return sl2::launch_g4<3, 2, 2, AK, BKM, ACC, 64, 128, 16>(st, g);                     \
+    case 24: return sl2::launch_g4<3, 4, 2, AK, BKM, ACC, 64, 128, 16>(st, g);                     \
     default: return -1;                                                                            \
   }
 
@@ -699,7 +701,7 @@ int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) 
 
 int gemm2_min_stages(int cfg) {
   return cfg == 15 || cfg == 16 || cfg == 20 ? 4 : cfg == 17 || cfg == 18 || cfg == 21 || cfg == 22 ? 2
-         : cfg == 19 || cfg == 23 ? 3 : 1;
+         : cfg == 19 || cfg == 23 || cfg == 24 ? 3 : 1;
 }
 
 void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
@@ -708,7 +710,7 @@ void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
       {256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256}, {256, 256},
       {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {128, 256},
       {256, 128}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {256, 128},
-      {256, 256}, {256, 256}, {256, 128}};
+      {256, 256}, {256, 256}, {256, 128}, {256, 128}};
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }

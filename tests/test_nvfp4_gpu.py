@@ -97,7 +97,7 @@ def test_fwd_dgrad_elementwise(T, n_in, n_out):
     assert e_y <= TOL_BF16 and e_dx <= TOL_BF16
 
 
-@pytest.mark.parametrize("cfg", range(24))
+@pytest.mark.parametrize("cfg", range(25))
 def test_tensor_scale_in_every_tile_config(monkeypatch, cfg):
     """The tensor scale is applied in each configuration's epilogue (forced via SL_GEMM_CONFIG)."""
     T, n_in, n_out = 1000, 2064, 520

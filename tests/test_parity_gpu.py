@@ -67,7 +67,7 @@ def test_fwd_dgrad_wgrad_elementwise(T, n_in, n_out):
     assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
 
 
-@pytest.mark.parametrize("cfg", range(24))
+@pytest.mark.parametrize("cfg", range(25))
 @pytest.mark.parametrize("T,n_in,n_out", [(300, 264, 520), (1000, 2056, 264), (2111, 1032, 776), (4104, 264, 520)])
 def test_every_tile_config(monkeypatch, cfg, T, n_in, n_out):
     """Each direct-to-LDS tile configuration, forced through SL_GEMM_CONFIG, on ragged shapes."""
