@@ -63,20 +63,31 @@ def parse():
     return p.parse_args()
 
 
+def kernel_sources_digest() -> str:
+    """sha256 over the kernel sources with their comments removed, so that a comment edit does
+    not void the counter records; any change to the code does."""
+    import glob
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "sharded_linear_amd", "csrc", "*"))):
+        text = open(f, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+        h.update(os.path.basename(f).encode() + b"\0" + code.encode())
+    return h.hexdigest()
+
+
 def stored_traffic(workload_key: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter record of this
     workload (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none or the kernel
     sources have changed since the counters were taken."""
-    import glob
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload_key}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "sharded_linear_amd", "csrc", "*"))):
-        h.update(open(f, "rb").read())
-    if h.hexdigest() != rec.get("kernel_sources_sha256"):
+    if kernel_sources_digest() != rec.get("kernel_sources_sha256"):
         return None
     b = rec.get("per_launch_bytes", {}).get(kernel)
     return None if b is None else int(b["fetch"] + b["write"])

@@ -15,7 +15,11 @@
 //    kb+j, so every result lane holds 4 consecutive k of one free index -- the MFMA layout.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16 (operand lane l: row/column l%32, k = 8*(l/32)+0..7; result
-// lane l holds column l%32, rows 8*(r/4) + 4*(l/32) + r%4).
+// lane l holds column l%32, rows 8*(r/4) + 4*(l/32) + r%4) and, in the default fixed-order
+// configurations, v_mfma_f32_16x16x32_bf16 (operand lane l: row/column l%16, k = 8*(l/16)+0..7;
+// result lane l holds column l%16, rows 4*(l/16) + r).  Both take the B fragment first, so each
+// accumulator block holds C^T and a lane owns one output row with four consecutive columns per
+// register quad (the epilogue in sl_epi.h relies on that).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -83,6 +87,7 @@ struct KMaj {
     }
   }
   // fragment of 32 rows starting at r0, k16 step ks: lane l gets row r0 + l%32, k 8(l/32)..+7
+  // (the compiler-scheduled kernels; the fixed-order ones compute offsets once, see kmaj_frag_off)
   __device__ static __forceinline__ bf16x8 frag(const char* lds, int r0, int ks, int lane) {
     const int r = r0 + (lane & 31);
     const int c = ks * 2 + (lane >> 5);
@@ -300,19 +305,20 @@ __global__ void __launch_bounds__(WGM * WGN * 64, OCC) gemm2(Gemm2Args g) {
   store_tile<WM, WN, TM, TN, ACC>(g, acc, smem, m0 + wm * WM, n0 + wn * WN, split, lane, wave);
 }
 
-// ---- 4-wave kernel with a fixed issue order ------------------------------------------------------
-// One wave per SIMD, each computing a 128x128 quarter of a 256x256 tile (16 accumulators), so a
-// k16 step is 16 MFMAs against 8 fragment reads.  The LDS ring holds S stages of 32 k; the loads
-// of stage s + S go out right after the barrier that ends the reads of stage s, so every load has
-// S - 1 stages of MFMA work to land.  Each k16 step interleaves its 16 MFMAs with the fragment
-// reads of the next step and, in a stage's second step, the HBM->LDS loads; sched_barrier fences
-// keep exactly that order.  The stage barrier sits between a stage's two steps: the second
-// step's fragments are already in registers, so its MFMAs cover the first reads of the next stage
-// issued just after the barrier, and no wave starts a stage waiting on LDS.
+// ---- kernels with a fixed issue order ------------------------------------------------------------
+// WGM x WGN waves (4 or 8), each computing a WM x WN part of a 256 x BN tile with TM x TN
+// accumulator blocks, so an MFMA step (k16 for 32x32 blocks, k32 for 16x16) is TM*TN MFMAs against
+// TM + TN fragment reads.  The LDS ring holds S stages of BK k; the loads of stage s + S go out
+// right after the barrier that ends the reads of stage s, so every load has S - 1 stages of MFMA
+// work to land.  Each step interleaves its MFMAs with the fragment reads of the next step and,
+// where due, the HBM->LDS loads; sched_barrier fences keep exactly that order.  The stage barrier
+// sits before a stage's last step: that step's fragments are already in registers, so its MFMAs
+// cover the first reads of the next stage issued just after the barrier, and no wave starts a
+// stage waiting on LDS.
 //
-// Barrier B(s+1), between the steps of stage s, certifies (i) every wave's loads of stage s + 1
+// Barrier B(s+1), before the last step of stage s, certifies (i) every wave's loads of stage s + 1
 // have landed (each wave waits for its own with vmcnt first) and (ii) every wave has read all of
-// stage s (its second-step fragments were waited for), so its slot can take stage s + S.
+// stage s (its last-step fragments were waited for), so its slot can take stage s + S.
 //
 // MF selects the matrix instruction: 32 for v_mfma_f32_32x32x16_bf16 (k16 steps, 32x32 blocks),
 // 16 for v_mfma_f32_16x16x32_bf16 (k32 steps, 16x16 blocks).  Both run at the same rate per clock,
