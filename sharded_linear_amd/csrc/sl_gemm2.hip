@@ -701,9 +701,19 @@ int launch_g4(hipStream_t st, Gemm2Args g) {
     default: return -1;                                                                            \
   }
 
+// SL2_PART splits the instantiations over separate compilations of this file (the build runs
+// them in parallel): 1 = fwd and the shared tables, 2 = dgrad, 3 = wgrad; unset = all.
+#if !defined(SL2_PART) || SL2_PART == 1
 int gemm2_fwd(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, true, false) }
+#endif
+#if !defined(SL2_PART) || SL2_PART == 2
 int gemm2_dgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(true, false, false) }
+#endif
+#if !defined(SL2_PART) || SL2_PART == 3
 int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) }
+#endif
+
+#if !defined(SL2_PART) || SL2_PART == 1
 
 int gemm2_min_stages(int cfg) {
   return cfg == 15 || cfg == 16 || cfg == 20 ? 4 : cfg == 17 || cfg == 18 || cfg == 21 || cfg == 22 ? 2
@@ -720,3 +730,4 @@ void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }
+#endif
