@@ -17,15 +17,15 @@
 // -127 (2^-127 is not a normal fp32 scale) takes a bit-field path instead: x times the exact fp32
 // power of two 2^127, rounded on the fp32 bit fields.  The GPU tests check every bf16 pattern.
 //
-// One workgroup quantises a 128 x 128 tile: each thread takes two 32-element row blocks straight
-// from HBM (16-byte loads; four threads cover 256 contiguous bytes of a row) and, for the
-// columnwise copy, stages them in LDS, from which each thread then reads two 32-row column
-// blocks.  Rowwise code stores are 32 contiguous bytes.  The columnwise codes go back into the
-// same LDS (the tile's four column blocks of one column make one 128-byte line of the transposed
-// output, 16-byte chunks XOR-swizzled by the column against bank conflicts) and leave as whole
-// lines, eight lanes to a line; each column's four scales leave as one dword.  Storing each column
-// block straight from its thread (32 bytes at a stride of R between lanes) cost about a fifth of
-// the kernel's time on [8192, 8192].
+// One workgroup quantises a 128 x 128 tile.  Each thread loads eight 16-byte chunks, 16 adjacent
+// lanes covering the 256 bytes of a tile row, so a quad of lanes holds one 32-element row block:
+// for the rowwise copy the quad shares the block's amax through two DPP quad permutes and each lane
+// stores the 8 codes of its chunk.  For the columnwise copy the tile is staged in LDS, from which
+// each thread reads two 32-row column blocks; their codes go back into the same LDS (a column's
+// four blocks make one 128-byte line of the transposed output, 16-byte chunks XOR-swizzled by the
+// column against bank conflicts) and leave as whole lines, eight lanes to a line, with each
+// column's four scales as one dword.  Storing each column block straight from its thread (32 bytes
+// at a stride of R between lanes) cost about a fifth of the kernel's time on [8192, 8192].
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -54,22 +54,28 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
-// Quantises one block of 32 bf16 elements, given as 16 words of two (element 2i in the low half of
-// word i): returns the biased scale and packs the codes into q[8] (code of element e in byte e).
-__device__ __forceinline__ uint32_t mx_block(const uint32_t (&w)[16], uint32_t (&q)[8]) {
-  // amax on the bit patterns: |bf16| orders like its 15-bit magnitude field
+// Largest magnitude field of N words of two bf16 elements: |bf16| orders like its 15-bit magnitude.
+template <int N>
+__device__ __forceinline__ uint32_t mag_max(const uint32_t (&w)[N]) {
   uint32_t m2 = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < N; ++i) {
     const uint32_t a = w[i] & 0x7FFF7FFFu;
     const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
     const uint32_t mlo = m2 & 0xFFFFu, mhi = m2 >> 16;
     m2 = (lo > mlo ? lo : mlo) | ((hi > mhi ? hi : mhi) << 16);
   }
-  const uint32_t amax = (m2 & 0xFFFFu) > (m2 >> 16) ? (m2 & 0xFFFFu) : (m2 >> 16);   // bf16 bits
+  return (m2 & 0xFFFFu) > (m2 >> 16) ? (m2 & 0xFFFFu) : (m2 >> 16);
+}
+
+// Encodes N words of two bf16 elements (element 2i in the low half of word i) of a block whose
+// amax has the bf16 bits `amax`: returns the biased scale and packs the codes into q[N / 2] (code of
+// element e in byte e).
+template <int N>
+__device__ __forceinline__ uint32_t mx_encode(const uint32_t (&w)[N], uint32_t amax, uint32_t (&q)[N / 2]) {
   if (amax == 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = 0;
+    for (int i = 0; i < N / 2; ++i) q[i] = 0;
     return 0;
   }
   int X = int((amax >> 7) & 0xFFu) - 127 - 8;          // floor(log2 amax) - 8 (bf16 exponent field)
@@ -77,7 +83,7 @@ __device__ __forceinline__ uint32_t mx_block(const uint32_t (&w)[16], uint32_t (
   if (X > -127) {
     const float scale = __uint_as_float(uint32_t(X + 127) << 23);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < N / 2; ++i) {
       s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16((s16x2){0, 0}, __builtin_bit_cast(bf16x2, w[2 * i]), scale, false);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, w[2 * i + 1]), scale, true);
       uint32_t c = __builtin_bit_cast(uint32_t, r);
@@ -88,7 +94,7 @@ __device__ __forceinline__ uint32_t mx_block(const uint32_t (&w)[16], uint32_t (
   } else {
     const float mult = __uint_as_float(0x7F000000u);     // 2^127, exact
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < N / 2; ++i) {
       uint32_t word = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -100,6 +106,19 @@ __device__ __forceinline__ uint32_t mx_block(const uint32_t (&w)[16], uint32_t (
     }
   }
   return uint32_t(X + 127);
+}
+
+// One block of 32 elements held by one thread.
+__device__ __forceinline__ uint32_t mx_block(const uint32_t (&w)[16], uint32_t (&q)[8]) {
+  return mx_encode(w, mag_max(w), q);
+}
+
+// Largest value of m over the four lanes of a quad (DPP quad permutes [1,0,3,2] and [2,3,0,1]).
+__device__ __forceinline__ uint32_t quad_max(uint32_t m) {
+  uint32_t o = uint32_t(__builtin_amdgcn_update_dpp(0, int(m), 0xB1, 0xF, 0xF, false));
+  m = o > m ? o : m;
+  o = uint32_t(__builtin_amdgcn_update_dpp(0, int(m), 0x4E, 0xF, 0xF, false));
+  return o > m ? o : m;
 }
 
 constexpr int kQT = 128;                 // tile edge
@@ -115,34 +134,26 @@ __global__ void __launch_bounds__(256) mx_quant_tile(const uint16_t* x, int64_t 
   uint8_t* const qbuf = reinterpret_cast<uint8_t*>(tile);
   uint8_t* const sbuf = qbuf + kQT * kQT;
   const int64_t r0 = int64_t(blockIdx.y) * kQT, c0 = int64_t(blockIdx.x) * kQT;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, ch = t & 15;       // 16-byte chunk of a tile row; a quad holds one block
+  uint4 raw[8];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int idx = t + 256 * h, row = idx >> 2, blk = idx & 3;
-    const int64_t gr = r0 + row, gc = c0 + blk * 32;
-    const bool valid = gr < R && gc < C;          // a whole row block (rowwise copies: C % 32 == 0)
-    uint4 raw[4];
+  for (int k = 0; k < 8; ++k) {                    // 8-element chunks (C % 8 == 0): all or nothing
+    const int64_t gr = r0 + (t >> 4) + 16 * k, gc = c0 + 8 * ch;
+    raw[k] = (gr < R && gc + 8 <= C) ? *reinterpret_cast<const uint4*>(x + gr * C + gc) : make_uint4(0, 0, 0, 0);
+  }
 #pragma unroll
-    for (int k = 0; k < 4; ++k)                    // 8-element chunks (C % 8 == 0): all or nothing
-      raw[k] = (gr < R && gc + 8 * k + 8 <= C) ? reinterpret_cast<const uint4*>(x + gr * C + gc)[k]
-                                               : make_uint4(0, 0, 0, 0);
-    if constexpr (COLS) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) reinterpret_cast<uint4*>(tile + row * kQStride + blk * 32)[k] = raw[k];
-    }
+  for (int k = 0; k < 8; ++k) {
+    const int row = (t >> 4) + 16 * k;
+    const int64_t gr = r0 + row, gc = c0 + 8 * ch;
+    if constexpr (COLS) reinterpret_cast<uint4*>(tile + row * kQStride)[ch] = raw[k];
     if constexpr (ROWS) {
-      if (valid) {
-        uint32_t v[16];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          v[4 * k] = raw[k].x; v[4 * k + 1] = raw[k].y; v[4 * k + 2] = raw[k].z; v[4 * k + 3] = raw[k].w;
-        }
-        uint32_t q[8];
-        const uint32_t s = mx_block(v, q);
-        uint4* dst = reinterpret_cast<uint4*>(qr + gr * C + gc);
-        dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
-        dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
-        sr[gr * (C / 32) + gc / 32] = uint8_t(s);
+      const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+      const uint32_t amax = quad_max(mag_max(w));  // every lane takes part; out-of-range chunks are 0
+      uint32_t q[2];
+      const uint32_t s = mx_encode(w, amax, q);
+      if (gr < R && gc < C) {                      // rowwise copies: C % 32 == 0, whole blocks
+        *reinterpret_cast<uint2*>(qr + gr * C + gc) = make_uint2(q[0], q[1]);
+        if ((ch & 3) == 0) sr[gr * (C / 32) + gc / 32] = uint8_t(s);
       }
     }
   }
