@@ -683,11 +683,16 @@ namespace {
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Block-scaled fp8 forward configuration: 256x256 tiles (8 waves) when they fill the chip, else
-// 128x128.  SL_F8_CONFIG="<n>" forces configuration n (0 or 1).
-int f8_config(int64_t T, int64_t out) {
+// 128x128.  SL_F8_CONFIG="<n>" forces configuration n (0: 256x256, 1: 128x128, 2: 256x128).
+int f8_config_override() {
   const char* e = getenv("SL_F8_CONFIG");
   const int cfg = (e && *e) ? atoi(e) : -1;
-  if (cfg == 0 || cfg == 1) return cfg;
+  return cfg >= 0 && cfg <= 2 ? cfg : -1;
+}
+
+int f8_config(int64_t T, int64_t out) {
+  const int cfg = f8_config_override();
+  if (cfg >= 0) return cfg;
   return ntiles(T, out, 256, 256) >= 200 ? 0 : 1;
 }
 
@@ -818,13 +823,17 @@ extern "C" int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, con
 
 namespace {
 
-// Split-K of the fp8 weight gradient (256x256 tiles, 128-k stages): fill ~256 CUs with output
-// tiles, keep at least 8 stages per split, at most 16 splits.
+// Tiles and split-K of the fp8 weight gradient (128-k stages).  256x256 tiles by default; where
+// they fill only about half the chip but 256x128 tiles fill it once, those run unsplit (no partial
+// planes, no reduce).  Otherwise split K to fill ~256 CUs with output tiles, keeping at least 8
+// stages per split and at most 16 splits.  SL_F8_CONFIG forces the tile configuration.
 F8Args f8_wgrad_plan(int64_t T, int64_t in, int64_t out) {
   F8Args g{};
   g.M = int(out); g.N = int(in); g.K = int(T);
-  g.cfg = 0;
-  const int64_t tiles = ntiles(out, in, 256, 256), nkt = T / 128;
+  const int64_t t256 = ntiles(out, in, 256, 256), t128 = ntiles(out, in, 256, 128);
+  const int forced = f8_config_override();
+  g.cfg = forced >= 0 ? forced : (t256 <= 144 && t128 >= 240 && t128 <= 288) ? 2 : 0;
+  const int64_t tiles = g.cfg == 0 ? t256 : g.cfg == 2 ? t128 : ntiles(out, in, 128, 128), nkt = T / 128;
   int64_t s = tiles < 200 ? (256 + tiles / 2) / tiles : 1;
   if (s > nkt / 8) s = nkt / 8;
   if (s > 16) s = 16;

@@ -296,6 +296,7 @@ int f8_fwd(hipStream_t st, F8Args g) {
   switch (g.cfg) {
     case 0: return sl2::launch_f8<256, 256, 2, 2, 4>(st, g);
     case 1: return sl2::launch_f8<128, 128, 3, 2, 2>(st, g);
+    case 2: return sl2::launch_f8<256, 128, 3, 4, 2>(st, g);
     default: return -1;
   }
 }
@@ -304,6 +305,7 @@ int f8_accum(hipStream_t st, F8Args g) {
   switch (g.cfg) {
     case 0: return sl2::launch_f8<256, 256, 2, 2, 4, true>(st, g);
     case 1: return sl2::launch_f8<128, 128, 3, 2, 2, true>(st, g);
+    case 2: return sl2::launch_f8<256, 128, 3, 4, 2, true>(st, g);
     default: return -1;
   }
 }

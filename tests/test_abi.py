@@ -128,11 +128,12 @@ def test_all_mxfp8_validation():
     assert w(None, A, A, A, A, A, 96, 64, 64, None, 0) == SL_ESHAPE               # T % 128
     assert w(None, A, A, None, A, A, 128, 64, 64, None, 0) == SL_EINVAL
     assert w(None, A, A, A, A, MIS, 128, 64, 64, None, 0) == SL_EALIGN
-    need = L.sl_mxfp8_wgrad_workspace_bytes(8192, 4096, 2048)                   # 128 tiles: split
-    assert need >= 2 * 2048 * 4096 * 4
-    assert w(None, A, A, A, A, A, 8192, 4096, 2048, None, 0) == SL_EWORKSPACE
-    assert w(None, A, A, A, A, A, 8192, 4096, 2048, A, need - 256) == SL_EWORKSPACE
+    need = L.sl_mxfp8_wgrad_workspace_bytes(8192, 2048, 1536)                   # 48 tiles: split
+    assert need >= 2 * 1536 * 2048 * 4
+    assert w(None, A, A, A, A, A, 8192, 2048, 1536, None, 0) == SL_EWORKSPACE
+    assert w(None, A, A, A, A, A, 8192, 2048, 1536, A, need - 256) == SL_EWORKSPACE
     assert L.sl_mxfp8_wgrad_workspace_bytes(8192, 2048, 8192) == 0              # 256 tiles: unsplit
+    assert L.sl_mxfp8_wgrad_workspace_bytes(8192, 4096, 2048) == 0              # 128 / 256 of 256x128: unsplit
     assert L.sl_mxfp8_wgrad_workspace_bytes(100, 64, 64) == 0
 
 

@@ -147,6 +147,38 @@ def test_fp8_wgrad_accum_elementwise(T, n_in, n_out):
     assert e <= TOL_F32
 
 
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_every_fp8_tile_config(monkeypatch, cfg):
+    """Each block-scaled fp8 tile configuration (256x256, 128x128, 256x128), forced through
+    SL_F8_CONFIG, on the forward, the dgrad and the split-K weight gradient of one ragged shape."""
+    T, n_in, n_out = 2176, 1152, 896                 # ragged against 256; 2 K splits in every configuration
+    say(f"case fp8 cfg={cfg} T={T} in={n_in} out={n_out}")
+    monkeypatch.setenv("SL_F8_CONFIG", str(cfg))
+    assert sl.sl_mxfp8_wgrad_workspace_bytes(T, n_in, n_out) == 2 * n_out * n_in * 4
+    X, W, dY = _quantised_case(T, n_in, n_out, 31 + cfg)
+    Xf, Wf, dYf = (numerics.bf16_bits_to_f64(a) for a in (X, W, dY))
+    Xq, Xs, XqT, XsT = sl.sl_mxfp8_quantize(dev_bf16(X))
+    Wq, Ws, WqT, WsT = sl.sl_mxfp8_quantize(dev_bf16(W))
+    dYq, dYs, dYqT, dYsT = sl.sl_mxfp8_quantize(dev_bf16(dY))
+    G0 = synth.normal_f32((n_out, n_in), 6)
+    G = torch.from_numpy(G0).cuda()
+    Y = sl.sl_linear_fwd_mxfp8(Xq, Xs, Wq, Ws)
+    dX = sl.sl_linear_dgrad_mxfp8(dYq, dYs, WqT, WsT)
+    sl.sl_linear_wgrad_accum_mxfp8(dYqT, dYsT, XqT, XsT, G)
+    torch.cuda.synchronize()
+    q, s_ = numerics.mx_quantize(Xf)
+    wq, ws = numerics.mx_quantize(Wf)
+    e_y = ol.rel_err(host_f64(Y), ol.linear_fwd_mxfp8(q, s_, wq, ws))
+    dq, ds = numerics.mx_quantize(dYf)
+    wqt, wst = numerics.mx_quantize_cols(Wf)
+    e_dx = ol.rel_err(host_f64(dX), ol.linear_dgrad_mxfp8(dq, ds, wqt, wst))
+    qd, sd = numerics.mx_quantize_cols(dYf)
+    qx, sx = numerics.mx_quantize_cols(Xf)
+    e_g = ol.rel_err(host_f64(G), ol.linear_wgrad_accum_mxfp8(G0, qd, sd, qx, sx))
+    say(f"  rel err Y {e_y:.2e} dX {e_dx:.2e} main_grad {e_g:.2e}")
+    assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
+
+
 def test_all_mxfp8_workload_sampled():
     """The all-MXFP8 workload at full size in the benchmark's launch configuration, two micro-batches:
     quantisation on the GPU, fwd / dgrad / wgrad on the block-scaled fp8 MFMA; Y and dX checked on
