@@ -13,6 +13,7 @@ figures (those events slow the step, so they stay out of the headline pass).
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -183,11 +184,14 @@ def main():
     # ---- one step --------------------------------------------------------------------------
     stream = torch.cuda.current_stream(dev)
     records = []        # (kind, flops, start_event, end_event) of the timed steps
+    pool = []           # events created before the kernel pass, which then only records them
+    counted = [0]       # launches per step, from a pass that launches nothing
 
     def launch(kind, flops, fn, *a, timed):
-        if timed:
-            s = torch.cuda.Event(enable_timing=True)
-            e = torch.cuda.Event(enable_timing=True)
+        if timed == "count":
+            counted[0] += 1
+        elif timed:
+            s, e = pool.pop(), pool.pop()
             s.record(stream)
             fn(*a)
             e.record(stream)
@@ -275,11 +279,19 @@ def main():
     ms = bounds[0].elapsed_time(bounds[-1]) / args.steps
     step_ms = sorted(bounds[k].elapsed_time(bounds[k + 1]) for k in range(args.steps))
     # Kernel pass: K more steps with HIP events around every launch on the launch stream, for the
-    # per-kernel durations and the roofline figures.
+    # per-kernel durations and the roofline figures.  The events are created beforehand and the
+    # garbage collector is paused: with up to 83 launches a step, creating two events per launch
+    # inside the pass slowed the host enough to let the GPU queue run dry inside some brackets.
     if not args.no_kernel_events:
-        for _ in range(args.steps):
-            step(timed=True)
-        torch.cuda.synchronize()
+        step(timed="count")
+        pool.extend(torch.cuda.Event(enable_timing=True) for _ in range(2 * counted[0] * args.steps))
+        gc.disable()
+        try:
+            for _ in range(args.steps):
+                step(timed=True)
+            torch.cuda.synchronize()
+        finally:
+            gc.enable()
     flops = w.flops_per_step()
     tflops = flops / (ms * 1e-3) / 1e12
     # MXFP8 workload: fwd runs block-scaled fp8 MFMA, dgrad/wgrad bf16 MFMA on the exactly
