@@ -110,8 +110,8 @@ def copy_calibration(nbytes: int) -> None:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's shard only: run it with --gpus 1 (multi-GPU collectives "
-              "are not part of this build)", file=sys.stderr)
+        print("bench.py measures one GPU's shard only: run it with --gpus 1 (the library has no "
+              "multi-GPU collectives)", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_calibration:
