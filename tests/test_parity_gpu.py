@@ -310,7 +310,7 @@ def test_mxfp8_elementwise(T, n_in, n_out):
     assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
 
 
-@pytest.mark.parametrize("cfg", range(2))
+@pytest.mark.parametrize("cfg", range(3))
 @pytest.mark.parametrize("T,n_in,n_out", [(300, 384, 520), (1000, 512, 776), (2050, 1024, 264), (4100, 256, 3336)])
 def test_mxfp8_fwd_every_config(monkeypatch, cfg, T, n_in, n_out):
     """Each block-scaled fp8 forward configuration, forced through SL_F8_CONFIG, on ragged M/N."""
