@@ -19,6 +19,11 @@
  *   - Arguments are validated on the host before any HIP call; on error nothing is launched.
  *   - Return value: SL_OK (0) or a negative SL_E* status; sl_status_str() names it.
  *   - Results of the GEMMs are deterministic: the same inputs give the same bits.
+ *   - Tile and split choices, and so the sizes the *_workspace_bytes queries return, can be forced
+ *     for tuning through the environment variables SL_GEMM_CONFIG and SL_SPLITK (bf16 GEMMs)
+ *     and SL_F8_CONFIG (block-scaled fp8 GEMMs).  Queries and calls read them at call time, so
+ *     keep them unchanged between a query and the calls whose workspace it sizes; a call that
+ *     finds its workspace too small returns SL_EWORKSPACE and launches nothing.
  */
 #ifndef SHARDED_LINEAR_H
 #define SHARDED_LINEAR_H
