@@ -179,6 +179,25 @@ def test_every_fp8_tile_config(monkeypatch, cfg):
     assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
 
 
+@pytest.mark.parametrize("T,n_in,n_out", [(2048, 1032, 776), (4096, 4096, 2048), (2048, 4096, 4096)])
+def test_fp8_wgrad_is_deterministic(T, n_in, n_out):
+    """The same weight gradient accumulated twice from the same main_grad gives the same bits:
+    split-K planes are summed in split order, and the unsplit plans (256x128 and 256x256 tiles)
+    do one read-modify-write per element."""
+    say(f"case fp8 wgrad determinism T={T} in={n_in} out={n_out} ws={sl.sl_mxfp8_wgrad_workspace_bytes(T, n_in, n_out)}")
+    X, _, dY = _quantised_case(T, n_in, n_out, 17 + T)
+    _, _, dYqT, dYsT = sl.sl_mxfp8_quantize(dev_bf16(dY), rows=False)
+    _, _, XqT, XsT = sl.sl_mxfp8_quantize(dev_bf16(X), rows=False)
+    G0 = torch.from_numpy(synth.normal_f32((n_out, n_in), 8)).cuda()
+    outs = []
+    for _ in range(2):
+        G = G0.clone()
+        sl.sl_linear_wgrad_accum_mxfp8(dYqT, dYsT, XqT, XsT, G)
+        outs.append(G)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+
+
 def test_all_mxfp8_workload_sampled():
     """The all-MXFP8 workload at full size in the benchmark's launch configuration, two micro-batches:
     quantisation on the GPU, fwd / dgrad / wgrad on the block-scaled fp8 MFMA; Y and dX checked on
