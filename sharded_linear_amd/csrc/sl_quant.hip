@@ -133,7 +133,9 @@ __global__ void __launch_bounds__(256) mx_quant_tile(const uint16_t* x, int64_t 
   // 16-byte stores and each column's scales as one group.
   uint8_t* const qbuf = reinterpret_cast<uint8_t*>(tile);
   uint8_t* const sbuf = qbuf + kQT * kQT;
-  const int64_t r0 = int64_t(blockIdx.y) * kQT, c0 = int64_t(blockIdx.x) * kQT;
+  // one-dimensional grid (row tiles can outnumber grid.y's 65535), column tile fastest
+  const int64_t ntc = (C + kQT - 1) / kQT;
+  const int64_t r0 = int64_t(blockIdx.x) / ntc * kQT, c0 = int64_t(blockIdx.x) % ntc * kQT;
   const int t = threadIdx.x, ch = t & 15;       // 16-byte chunk of a tile row; a quad holds one block
   uint4 raw[8];
 #pragma unroll
@@ -203,7 +205,7 @@ __global__ void __launch_bounds__(256) mx_quant_tile(const uint16_t* x, int64_t 
 int mx_quantize(hipStream_t st, const void* x, int64_t R, int64_t C, uint8_t* qr, uint8_t* sr, uint8_t* qc,
                 uint8_t* sc) {
   if (R == 0 || C == 0 || (!qr && !qc)) return 0;
-  const dim3 grid(unsigned((C + sl2::kQT - 1) / sl2::kQT), unsigned((R + sl2::kQT - 1) / sl2::kQT));
+  const dim3 grid(unsigned(((C + sl2::kQT - 1) / sl2::kQT) * ((R + sl2::kQT - 1) / sl2::kQT)));
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   if (qr && qc) hipLaunchKernelGGL((sl2::mx_quant_tile<true, true>), grid, dim3(256), 0, st, xp, R, C, qr, sr, qc, sc);
   else if (qr) hipLaunchKernelGGL((sl2::mx_quant_tile<true, false>), grid, dim3(256), 0, st, xp, R, C, qr, sr, qc, sc);

@@ -58,6 +58,23 @@ def test_quantise_bit_exact(R, C):
     assert np.array_equal(qc.cpu().numpy(), wqc) and np.array_equal(sc.cpu().numpy(), wsc)
 
 
+def test_quantise_beyond_65535_row_tiles():
+    """2^23 + 32 rows (65537 row tiles of 128): both copies, checked against the oracle on the
+    first rows and on the row blocks around 2^23.  The matrix repeats a [4096, 32] block."""
+    R, C = (1 << 23) + 32, 32
+    say(f"case quantise R={R} C={C}")
+    bits = np.tile(_bf16_case(4096, C, 5), ((R + 4095) // 4096, 1))[:R]
+    qr, sr, qc, sc = sl.sl_mxfp8_quantize(dev_bf16(bits))
+    torch.cuda.synchronize()
+    for lo, hi in ((0, 128), ((1 << 23) - 96, R)):
+        xf = numerics.bf16_bits_to_f64(bits[lo:hi])
+        wqr, wsr = numerics.mx_quantize(xf)
+        wqc, wsc = numerics.mx_quantize_cols(xf)
+        assert np.array_equal(qr[lo:hi].cpu().numpy(), wqr) and np.array_equal(sr[lo:hi].cpu().numpy(), wsr)
+        assert np.array_equal(qc[:, lo:hi].cpu().numpy(), wqc)
+        assert np.array_equal(sc[:, lo // 32:hi // 32].cpu().numpy(), wsc)
+
+
 @pytest.mark.parametrize("shuffle", [False, True])
 def test_quantise_every_bf16_pattern(shuffle):
     """Every finite bf16 bit pattern, laid out as a [2048, 32] matrix (in order, or shuffled so
