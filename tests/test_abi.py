@@ -135,6 +135,9 @@ def test_all_mxfp8_validation():
     assert L.sl_mxfp8_wgrad_workspace_bytes(8192, 2048, 8192) == 0              # 256 tiles: unsplit
     assert L.sl_mxfp8_wgrad_workspace_bytes(8192, 4096, 2048) == 0              # 128 / 256 of 256x128: unsplit
     assert L.sl_mxfp8_wgrad_workspace_bytes(100, 64, 64) == 0
+    # code operands of 2 GiB or more are beyond the direct loads of the both-MXFP8 kernels
+    assert d(None, A, A, A, A, A, 1 << 20, 128, 4096) == SL_ESHAPE               # dYq 4 GiB
+    assert w(None, A, A, A, A, A, 1 << 20, 64, 4096, None, 0) == SL_ESHAPE       # dYqT 4 GiB
 
 
 def test_nvfp4_validation():

@@ -197,6 +197,25 @@ def test_operand_beyond_direct_load_extent(which):
         assert ol.rel_err(host_f64(G), ref) <= TOL_F32
 
 
+def test_mxfp8_fwd_operand_beyond_direct_load_extent():
+    """MXFP8 forward with Xq of 2 GiB or more: the block-scaled kernel's direct loads cannot
+    address it, so the call runs on the register-staged kernel that dequantises on load.  Xq
+    repeats a seeded block of P rows (plus a ragged tail of R rows); Y is checked on sampled rows."""
+    P, reps, R = 4096, 64, 520
+    T, n_in, n_out = P * reps + R, 8192, 64          # 262,664 x 8192 codes = 2.15 GB
+    say(f"case big mxfp8 fwd: T={T} in={n_in} out={n_out}")
+    Xb, Sb = synth.mxfp8_normal((P, n_in), 7011)
+    Wq, Ws = synth.mxfp8_normal((n_out, n_in), 7012, synth.W_STD)
+    xd, sd = dev_u8(Xb), dev_u8(Sb)
+    Xq = torch.cat([xd.repeat(reps, 1), xd[:R]], dim=0)
+    Xs = torch.cat([sd.repeat(reps, 1), sd[:R]], dim=0)
+    Y = sl.sl_linear_fwd_mxfp8(Xq, Xs, dev_u8(Wq), dev_u8(Ws))
+    torch.cuda.synchronize()
+    rows = np.r_[0:40, P * 17 + 5:P * 17 + 45, T - 40:T]
+    ref = ol.linear_fwd_mxfp8(Xb[rows % P], Sb[rows % P], Wq, Ws)
+    assert ol.rel_err(host_f64(Y[torch.as_tensor(rows, device="cuda")]), ref) <= TOL_BF16
+
+
 def test_neighbours_and_padding_untouched():
     """A wgrad into one view of grad_data leaves every other element bit-identical."""
     say("case neighbours and padding")
