@@ -19,11 +19,11 @@
  *   - Arguments are validated on the host before any HIP call; on error nothing is launched.
  *   - Return value: SL_OK (0) or a negative SL_E* status; sl_status_str() names it.
  *   - Results of the GEMMs are deterministic: the same inputs give the same bits.
- *   - Tile and split choices, and so the sizes the *_workspace_bytes queries return, can be forced
- *     for tuning through the environment variables SL_GEMM_CONFIG and SL_SPLITK (bf16 GEMMs)
- *     and SL_F8_CONFIG (block-scaled fp8 GEMMs).  Queries and calls read them at call time, so
- *     keep them unchanged between a query and the calls whose workspace it sizes; a call that
- *     finds its workspace too small returns SL_EWORKSPACE and launches nothing.
+ *   - Tile and split choices, and so the sizes the *_workspace_bytes queries return, are the
+ *     library's own unless forced through sl_set_tuning(); the library reads no environment
+ *     variables.  Keep the knobs unchanged between a query and the calls whose workspace it
+ *     sizes; a call that finds its workspace too small returns SL_EWORKSPACE and launches
+ *     nothing.
  */
 #ifndef SHARDED_LINEAR_H
 #define SHARDED_LINEAR_H
@@ -47,6 +47,28 @@ enum {
 
 /* Name of a status code (static storage). */
 const char* sl_status_str(int status);
+
+/* ---------------------------------------------------------------------------------------------
+ * Tuning knobs, for measurement and tests (not needed for correct use).  sl_set_tuning forces
+ * one choice for every later call and workspace query of this process; value -1 restores the
+ * built-in choice.  The previous value is stored in *previous when it is not NULL.  Ranges:
+ *   SL_TUNE_{FWD,DGRAD,WGRAD}_CONFIG  bf16 tile configuration 0..24 of that product
+ *   SL_TUNE_SPLITK                    split count 1..64 of the bf16 weight gradient
+ *   SL_TUNE_F8_CONFIG                 block-scaled fp8 configuration 0..2 (0: 256x256, 1: 128x128,
+ *                                     2: 256x128), for the weight gradient as well
+ * An unknown knob or a value out of range returns SL_EINVAL and changes nothing.  The knobs are
+ * process-wide atomics: safe to set from any thread, but a call that overlaps a change may see
+ * either value, so change them only while no call is being planned.
+ * ------------------------------------------------------------------------------------------- */
+enum {
+  SL_TUNE_FWD_CONFIG = 0,
+  SL_TUNE_DGRAD_CONFIG = 1,
+  SL_TUNE_WGRAD_CONFIG = 2,
+  SL_TUNE_SPLITK = 3,
+  SL_TUNE_F8_CONFIG = 4,
+  SL_TUNE_COUNT = 5
+};
+int sl_set_tuning(int32_t knob, int32_t value, int32_t* previous);
 
 /* ---------------------------------------------------------------------------------------------
  * Buffer layout (host only; llm-infra-atlas "05 · grad/param buffer", sections 4.1-4.3 and 5).

@@ -21,6 +21,7 @@ P_I32 = ctypes.POINTER(ctypes.c_int32)
 # name -> (restype, argtypes); mirrors include/sharded_linear.h
 PROTOTYPES = {
     "sl_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "sl_set_tuning": (ctypes.c_int, [c_i32, c_i32, P_I32]),
     "sl_layout_build": (ctypes.c_int, [c_i32, P_I64, c_i64, c_i64, c_i64, P_I64, P_I64, P_I32, c_i32,
                                        P_I64, P_I64, P_I64, P_I32, P_I64]),
     "sl_default_bucket_size": (c_i64, [c_i64]),

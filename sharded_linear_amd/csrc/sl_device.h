@@ -2,10 +2,24 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
 namespace sl2 {
+
+// Host: hipFuncSetAttribute(MaxDynamicSharedMemorySize) of one kernel, once per device.  `done`
+// (one per kernel) holds a bit per device id; ids of 64 and above set the attribute at every
+// launch.  Two threads that race on the first launch both set the same value, which is harmless.
+inline int smem_attr_once(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -5;
+  const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return 0;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) return -5;
+  if (bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return 0;
+}
 
 template <int I>
 using ic = std::integral_constant<int, I>;

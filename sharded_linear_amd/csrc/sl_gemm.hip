@@ -27,6 +27,7 @@
 // of main_grad.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -381,24 +382,19 @@ constexpr int64_t kMaxDmaBytes = 0x7FFFFFF0LL - 16;
 
 int64_t ntiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
-// Tuning overrides.  SL_GEMM_CONFIG="<n>" forces tile configuration n for every bf16 GEMM, or
-// "fwd=<n>,dgrad=<n>,wgrad=<n>" per GEMM; SL_SPLITK="<n>" forces the weight gradient's split
-// count.  Unset (or out of range) keeps the built-in choice.
+// Tuning overrides, set through sl_set_tuning (-1: the built-in choice).  Process-wide and read
+// with relaxed loads: a query and the calls it sizes see the same values unless the caller
+// changes them in between.
+std::atomic<int> g_tune[SL_TUNE_COUNT] = {{-1}, {-1}, {-1}, {-1}, {-1}};
+
 int config_override(Kind k) {
-  const char* e = getenv("SL_GEMM_CONFIG");
-  if (!e || !*e) return -1;
-  const char* key = k == Kind::Fwd ? "fwd=" : k == Kind::Dgrad ? "dgrad=" : "wgrad=";
-  const char* p = strstr(e, key);
-  int v = -1;
-  if (p) v = atoi(p + strlen(key));
-  else if (!strchr(e, '=')) v = atoi(e);
-  return (v >= 0 && v < kGemm2Configs) ? v : -1;
+  return g_tune[k == Kind::Fwd ? SL_TUNE_FWD_CONFIG : k == Kind::Dgrad ? SL_TUNE_DGRAD_CONFIG : SL_TUNE_WGRAD_CONFIG]
+      .load(std::memory_order_relaxed);
 }
 
 int splits_override() {
-  const char* e = getenv("SL_SPLITK");
-  const int v = (e && *e) ? atoi(e) : 0;
-  return (v >= 1 && v <= 64) ? v : 0;
+  const int v = g_tune[SL_TUNE_SPLITK].load(std::memory_order_relaxed);
+  return v > 0 ? v : 0;
 }
 
 // Tile configuration for a forward / dgrad GEMM: each candidate's time is estimated as the number
@@ -591,6 +587,16 @@ int linear_dgrad(hipStream_t hs, const void* dY, const void* W, float alpha, voi
 
 }  // namespace
 
+extern "C" int sl_set_tuning(int32_t knob, int32_t value, int32_t* previous) {
+  static const int hi[SL_TUNE_COUNT] = {kGemm2Configs - 1, kGemm2Configs - 1, kGemm2Configs - 1, 64, 2};
+  static const int lo[SL_TUNE_COUNT] = {0, 0, 0, 1, 0};
+  if (knob < 0 || knob >= SL_TUNE_COUNT) return SL_EINVAL;
+  if (value != -1 && (value < lo[knob] || value > hi[knob])) return SL_EINVAL;
+  const int old = g_tune[knob].exchange(value);
+  if (previous) *previous = old;
+  return SL_OK;
+}
+
 extern "C" int sl_grad_buffer_zero(void* stream, float* grad_data, int64_t numel) {
   if (numel < 0) return SL_EINVAL;
   if (numel == 0) return SL_OK;
@@ -683,12 +689,8 @@ namespace {
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Block-scaled fp8 forward configuration: 256x256 tiles (8 waves) when they fill the chip, else
-// 128x128.  SL_F8_CONFIG="<n>" forces configuration n (0: 256x256, 1: 128x128, 2: 256x128).
-int f8_config_override() {
-  const char* e = getenv("SL_F8_CONFIG");
-  const int cfg = (e && *e) ? atoi(e) : -1;
-  return cfg >= 0 && cfg <= 2 ? cfg : -1;
-}
+// 128x128.  The SL_TUNE_F8_CONFIG knob forces configuration n (0: 256x256, 1: 128x128, 2: 256x128).
+int f8_config_override() { return g_tune[SL_TUNE_F8_CONFIG].load(std::memory_order_relaxed); }
 
 int f8_config(int64_t T, int64_t out) {
   const int cfg = f8_config_override();
@@ -801,8 +803,12 @@ extern "C" int sl_linear_wgrad_accum_mxfp8x(void* stream, const uint8_t* Xq, con
   if (!aligned16(Xq) || !aligned16(dY) || !aligned16(main_grad)) return SL_EALIGN;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (mx_bf16_path(T, in, T * out * 2)) {
+    // the whole workspace (dequantised X, then the bf16 plan's split planes) is checked before
+    // the first launch
     const int64_t xb = round256(T * in * 2);
-    if (!workspace || !aligned16(workspace) || workspace_bytes < size_t(xb)) return SL_EWORKSPACE;
+    const Plan p = make_plan(Kind::Wgrad, false, out, in, T, T * out * 2, T * in * 2);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < size_t(xb) + plan_ws_bytes(p, out, in))
+      return SL_EWORKSPACE;
     if (mx_dequant(hs, Xq, Xs, workspace, T, in)) return SL_EHIP;
     return sl_linear_wgrad_accum(stream, workspace, dY, main_grad, T, in, out, static_cast<char*>(workspace) + xb,
                                  workspace_bytes - size_t(xb));
@@ -826,7 +832,7 @@ namespace {
 // Tiles and split-K of the fp8 weight gradient (128-k stages).  256x256 tiles by default; where
 // they fill only about half the chip but 256x128 tiles fill it once, those run unsplit (no partial
 // planes, no reduce).  Otherwise split K to fill ~256 CUs with output tiles, keeping at least 8
-// stages per split and at most 16 splits.  SL_F8_CONFIG forces the tile configuration.
+// stages per split and at most 16 splits.  The SL_TUNE_F8_CONFIG knob forces the tile configuration.
 F8Args f8_wgrad_plan(int64_t T, int64_t in, int64_t out) {
   F8Args g{};
   g.M = int(out); g.N = int(in); g.K = int(T);

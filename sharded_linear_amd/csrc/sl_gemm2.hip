@@ -611,12 +611,8 @@ int launch_cfg(hipStream_t st, Gemm2Args g) {
   constexpr int epi = WGM * WGN * EpiOf<BM / WGM, BN / WGN, ACC>::kBytes;
   constexpr int lds = ring > epi ? ring : epi;
   auto kfn = gemm2<BM, BN, BK, S, WGM, WGN, A_KM, B_KM, ACC, SCHED, OCC>;
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-      return -5;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr{0};
+  if (smem_attr_once(reinterpret_cast<const void*>(kfn), lds, attr)) return -5;
   g.tiles_m = (g.M + BM - 1) / BM;
   g.tiles_n = (g.N + BN - 1) / BN;
   hipLaunchKernelGGL(kfn, dim3(g.tiles_m * g.tiles_n, 1, g.splits), dim3(WGM * WGN * 64), lds, st, g);
@@ -627,12 +623,8 @@ template <int S, int WGM, int WGN, bool A_KM, bool B_KM, bool ACC, int BK = 32, 
 int launch_g4(hipStream_t st, Gemm2Args g) {
   using P = G4<A_KM, B_KM, ACC, S, WGM, WGN, BK, BN, MF>;
   auto kfn = gemm4<A_KM, B_KM, ACC, S, WGM, WGN, BK, BN, MF>;
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, P::kLds) != hipSuccess)
-      return -5;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr{0};
+  if (smem_attr_once(reinterpret_cast<const void*>(kfn), P::kLds, attr)) return -5;
   // every split needs at least S stages of 32 k: the prologue fills the whole ring (the planner
   // gives shorter products to another configuration)
   const int nkt = (g.K + P::BK - 1) / P::BK;

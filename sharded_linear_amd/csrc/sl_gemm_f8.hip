@@ -278,12 +278,8 @@ int launch_f8(hipStream_t st, F8Args g) {
   constexpr int lds = ring > epi ? ring : epi;
   static_assert(lds <= 160 * 1024, "LDS");
   auto kfn = gemm_f8fwd<BM, BN, S, WGM, WGN, ACC>;
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-      return -5;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr{0};
+  if (smem_attr_once(reinterpret_cast<const void*>(kfn), lds, attr)) return -5;
   g.tiles_m = (g.M + BM - 1) / BM;
   g.tiles_n = (g.N + BN - 1) / BN;
   hipLaunchKernelGGL(kfn, dim3(g.tiles_m * g.tiles_n, 1, ACC ? g.splits : 1), dim3(WGM * WGN * 64), lds, st, g);

@@ -6,6 +6,7 @@ stream of that device.  Outputs not supplied are allocated with torch.empty (plu
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 
 import torch
@@ -40,6 +41,34 @@ def _device(t):
     if not t.is_cuda:
         raise ValueError("the HIP library works on GPU tensors only; got a CPU tensor")
     return t.device
+
+
+# knobs of sl_set_tuning, in the order of the header's SL_TUNE_* enum
+TUNE_KNOBS = {"fwd": 0, "dgrad": 1, "wgrad": 2, "splitk": 3, "f8": 4}
+
+
+def sl_set_tuning(knob: str, value: int) -> int:
+    """Force a tuning choice (-1 restores the built-in one); returns the previous value."""
+    prev = ctypes.c_int32(0)
+    check("sl_set_tuning", lib().sl_set_tuning(TUNE_KNOBS[knob], int(value), ctypes.byref(prev)))
+    return prev.value
+
+
+@contextlib.contextmanager
+def tuning(**knobs):
+    """Within the block, force the given knobs (names of TUNE_KNOBS; ``gemm=n`` sets the tile
+    configuration of all three bf16 products); the previous values come back on exit."""
+    if "gemm" in knobs:
+        cfg = knobs.pop("gemm")
+        knobs = {"fwd": cfg, "dgrad": cfg, "wgrad": cfg, **knobs}
+    saved = []
+    try:
+        for k, v in knobs.items():
+            saved.append((k, sl_set_tuning(k, v)))
+        yield
+    finally:
+        for k, v in reversed(saved):
+            sl_set_tuning(k, v)
 
 
 def sl_grad_buffer_zero(grad_data: torch.Tensor) -> torch.Tensor:

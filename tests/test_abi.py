@@ -186,3 +186,61 @@ def test_python_binding_rejects_cpu_tensors():
     from sharded_linear_amd import sl_linear_fwd
     with pytest.raises(ValueError):
         sl_linear_fwd(torch.zeros(4, 8, dtype=torch.bfloat16), torch.zeros(8, 8, dtype=torch.bfloat16))
+
+
+def test_tuning_knobs_and_workspace_query_agree():
+    """A forced split count or tile configuration changes the workspace query and the call's check
+    alike (the call refuses the default-sized workspace under a forced larger split), and -1
+    restores the built-in choices; unknown knobs and out-of-range values are refused."""
+    L = _lib.lib()
+    ws = L.sl_wgrad_workspace_bytes
+    f = L.sl_linear_wgrad_accum
+    T, n_in, n_out = 8192, 2048, 1536                  # 48 tiles of 256x256: split by default
+    plane = n_in * n_out * 4
+    default = ws(T, n_in, n_out)
+    assert default > 0 and default % plane == 0
+    prev = ctypes.c_int32(99)
+    try:
+        assert L.sl_set_tuning(3, 7, ctypes.byref(prev)) == SL_OK and prev.value == -1
+        assert ws(T, n_in, n_out) == 7 * plane
+        assert f(None, A, A, A, T, n_in, n_out, A, default) == SL_EWORKSPACE     # sized for the default
+        assert L.sl_set_tuning(3, 1, None) == SL_OK
+        assert ws(T, n_in, n_out) == 0                                             # forced unsplit
+        assert L.sl_set_tuning(3, -1, ctypes.byref(prev)) == SL_OK and prev.value == 1
+        assert ws(T, n_in, n_out) == default
+        # a forced 256x128 configuration (cfg 20) changes the weight gradient's tile count
+        assert L.sl_set_tuning(2, 20, None) == SL_OK
+        forced = ws(T, n_in, n_out)
+        assert forced % plane == 0 and forced != default
+        assert L.sl_set_tuning(2, -1, None) == SL_OK
+        assert ws(T, n_in, n_out) == default
+        # validation: knob range and value ranges; a refused call changes nothing
+        assert L.sl_set_tuning(5, 0, None) == SL_EINVAL and L.sl_set_tuning(-1, 0, None) == SL_EINVAL
+        assert L.sl_set_tuning(0, 25, None) == SL_EINVAL and L.sl_set_tuning(3, 0, None) == SL_EINVAL
+        assert L.sl_set_tuning(3, 65, None) == SL_EINVAL and L.sl_set_tuning(4, 3, None) == SL_EINVAL
+        assert L.sl_set_tuning(4, -2, None) == SL_EINVAL
+        assert ws(T, n_in, n_out) == default
+    finally:
+        for k in range(5):
+            L.sl_set_tuning(k, -1, None)
+
+
+def test_tuning_environment_variables_are_not_read(monkeypatch):
+    """The library reads no environment variables: the old tuning names change nothing."""
+    ws = _lib.lib().sl_wgrad_workspace_bytes
+    default = ws(8192, 2048, 1536)
+    for name, val in (("SL_SPLITK", "7"), ("SL_GEMM_CONFIG", "20"), ("SL_F8_CONFIG", "1")):
+        monkeypatch.setenv(name, val)
+    assert ws(8192, 2048, 1536) == default
+
+
+def test_mxfp8x_checks_the_whole_workspace_before_launching():
+    """The dequantised-X wgrad checks dequantised operand + split planes before its first launch:
+    a workspace that holds only the dequantised X is refused on a split shape."""
+    L = _lib.lib()
+    T, n_in, n_out = 8192, 2048, 1536
+    xb = (T * n_in * 2 + 255) // 256 * 256
+    need = L.sl_mxfp8_workspace_bytes(T, n_in, n_out)
+    assert need > xb                                          # the planes follow the operand
+    assert L.sl_linear_wgrad_accum_mxfp8x(None, A, A, A, A, T, n_in, n_out, A, xb) == SL_EWORKSPACE
+    assert L.sl_linear_wgrad_accum_mxfp8x(None, A, A, A, A, T, n_in, n_out, A, need - 256) == SL_EWORKSPACE

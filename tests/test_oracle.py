@@ -149,6 +149,28 @@ def test_exact_special_cases():
     assert np.array_equal(linear.linear_wgrad_accum(np.zeros((7, 5)), x1, g1), np.outer(g1[0], x1[0]))
 
 
+def test_non_finite_inputs_propagate_as_the_definition_says():
+    """The oracle's products on NaN / inf inputs agree with the brute-force loops entry by entry
+    (NaN where a NaN term or +inf and -inf terms meet, +-inf where only infinite terms of one sign
+    do), so it can serve as the reference for non-finite propagation."""
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((5, 6)); W = rng.standard_normal((4, 6)); dY = rng.standard_normal((5, 4))
+    G0 = rng.standard_normal((4, 6))
+    X[1, 2] = np.nan; X[3, 4] = np.inf; dY[0, 1] = -np.inf; dY[2, 3] = np.nan; G0[2, 5] = np.inf
+    with np.errstate(invalid="ignore"):
+        pairs = [(linear.linear_fwd(X, W), linear.fwd_brute(X, W)),
+                 (linear.linear_dgrad(dY, W), linear.dgrad_brute(dY, W)),
+                 (linear.linear_wgrad_accum(G0, X, dY), linear.wgrad_accum_brute(G0, X, dY))]
+    for got, want in pairs:
+        assert np.array_equal(np.isnan(got), np.isnan(want))
+        assert np.array_equal(np.isinf(got), np.isinf(want))
+        inf = np.isinf(want)
+        assert np.array_equal(np.sign(got[inf]), np.sign(want[inf]))
+        fin = np.isfinite(want)
+        np.testing.assert_allclose(got[fin], want[fin], rtol=1e-12, atol=1e-12)
+    assert np.isnan(pairs[0][0][1]).all() and np.isnan(pairs[2][0][:, 2]).all()
+
+
 def test_power_of_two_scaling_is_exact():
     rng = np.random.default_rng(4)
     X, W, dY = rng.standard_normal((9, 6)), rng.standard_normal((4, 6)), rng.standard_normal((9, 4))
@@ -563,3 +585,141 @@ def test_nvfp4_weight_products_brute_force(T, n_in, n_out):
                                linear.fwd_brute(numerics.bf16_bits_to_f64(X), W), rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(linear.linear_dgrad_nvfp4w(dY, packed, scales, t),
                                linear.dgrad_brute(numerics.bf16_bits_to_f64(dY), W), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# The parity metric: max|got - ref| / max|ref| over one tensor
+# ---------------------------------------------------------------------------------------------
+
+def _rel_err_cases():
+    """(got, ref, value) triples worked by hand."""
+    return [
+        # the largest |ref| is negative and the largest |got - ref| has a negative sign:
+        # |diff| = [0, 2, 1] -> 2; max|ref| = 4 -> 0.5
+        (np.array([1.0, -6.0, 3.0]), np.array([1.0, -4.0, 2.0]), 0.5),
+        # two-dimensional: the maxima are taken over every entry, not per row
+        (np.array([[0.0, 1.0], [3.0, 3.5]]), np.array([[0.0, 2.0], [-8.0, 3.0]]), 11.0 / 8.0),
+        # identical tensors
+        (np.array([[-1.5, 2.0]]), np.array([[-1.5, 2.0]]), 0.0),
+        # both all-zero: no error
+        (np.zeros((3, 2)), np.zeros((3, 2)), 0.0),
+        # empty tensors
+        (np.zeros((0, 4)), np.zeros((0, 4)), 0.0),
+    ]
+
+
+def test_rel_err_hand_computed_values():
+    for got, ref, want in _rel_err_cases():
+        assert linear.rel_err(got, ref) == want, (got, ref)
+    # a nonzero result against an all-zero reference can pass no bar
+    assert linear.rel_err(np.array([0.0, 1e-30]), np.zeros(2)) == math.inf
+    # a power-of-two rescaling of both sides, or a joint sign flip, leaves the metric unchanged
+    got, ref, want = _rel_err_cases()[0]
+    assert linear.rel_err(-4.0 * got, -4.0 * ref) == want
+
+
+def test_rel_err_non_finite_results_fail_every_bar():
+    ref = np.array([1.0, -2.0, 0.5])
+    for bad in (np.nan, np.inf, -np.inf):
+        got = ref.copy()
+        got[1] = bad
+        e = linear.rel_err(got, ref)
+        assert not (e <= 4e-3) and not (e <= 1e-4), (bad, e)
+
+
+def test_rel_err_pins_catch_planted_slips():
+    """Plausible mistakes in the metric each fail one of the hand-worked cases above."""
+    def dropped_abs(got, ref):
+        return float(np.max(got - ref) / np.max(np.abs(ref)))
+
+    def mean_denominator(got, ref):
+        return float(np.max(np.abs(got - ref)) / np.mean(np.abs(ref)))
+
+    def signed_denominator(got, ref):
+        return float(np.max(np.abs(got - ref)) / np.max(ref))
+
+    def zero_ref_passes(got, ref):
+        den = np.max(np.abs(ref))
+        return 0.0 if den == 0 else float(np.max(np.abs(got - ref)) / den)
+
+    for slip in (dropped_abs, mean_denominator, signed_denominator):
+        assert any(slip(g, r) != v for g, r, v in _rel_err_cases()[:2]), slip.__name__
+    assert zero_ref_passes(np.array([0.0, 1e-30]), np.zeros(2)) != math.inf
+
+
+# ---------------------------------------------------------------------------------------------
+# MXFP8-operand products ([GTP] section 1.3: E4M3 elements, one E8M0 scale per 32 elements)
+# ---------------------------------------------------------------------------------------------
+
+def _mx_scalar(codes, scales, r, c):
+    """One MXFP8 element by the scalar definitions: E4M3(code) * 2^(scale of block c // 32 - 127)."""
+    return numerics.e4m3_value(int(codes[r, c])) * 2.0 ** (int(scales[r, c // 32]) - 127)
+
+
+def _mx_operands(T, n_in, n_out, seed):
+    """Random finite codes; X and W scales from disjoint ranges that also differ block to block,
+    so a swapped, transposed or mis-indexed scale array changes the products."""
+    rng = np.random.default_rng(seed)
+    Xq = rng.integers(0, 256, (T, n_in), dtype=np.uint8)
+    Wq = rng.integers(0, 256, (n_out, n_in), dtype=np.uint8)
+    for q in (Xq, Wq):
+        q[(q & 0x7F) == 0x7F] = 0x3A                           # no NaN codes
+    Xs = rng.integers(118, 124, (T, n_in // 32), dtype=np.uint8)
+    Ws = rng.integers(128, 134, (n_out, n_in // 32), dtype=np.uint8)
+    dY = synth.f32_to_bf16_bits(rng.standard_normal((T, n_out)).astype(np.float32))
+    G0 = rng.standard_normal((n_out, n_in))
+    return Xq, Xs, Wq, Ws, dY, G0
+
+
+def _mx_brute(Xq, Xs, Wq, Ws, dY, G0):
+    """fwd, dgrad and wgrad-accumulate as triple loops over elements decoded one at a time."""
+    T, n_in = Xq.shape
+    n_out = Wq.shape[0]
+    X = np.array([[_mx_scalar(Xq, Xs, t, i) for i in range(n_in)] for t in range(T)])
+    W = np.array([[_mx_scalar(Wq, Ws, o, i) for i in range(n_in)] for o in range(n_out)])
+    d = numerics.bf16_bits_to_f64(dY)
+    Y = np.array([[sum(X[t, i] * W[o, i] for i in range(n_in)) for o in range(n_out)] for t in range(T)])
+    dX = np.array([[sum(d[t, o] * W[o, i] for o in range(n_out)) for i in range(n_in)] for t in range(T)])
+    G = np.array([[G0[o, i] + sum(d[t, o] * X[t, i] for t in range(T)) for i in range(n_in)]
+                  for o in range(n_out)])
+    return Y, dX, G
+
+
+def _mx_matches(fwd, dgrad, wgrad, case):
+    Xq, Xs, Wq, Ws, dY, G0 = case
+    Y, dX, G = _mx_brute(*case)
+    close = lambda a, b: np.allclose(a, b, rtol=1e-12, atol=1e-12)   # noqa: E731
+    return (close(fwd(Xq, Xs, Wq, Ws), Y), close(dgrad(dY, Wq, Ws), dX),
+            close(wgrad(G0, Xq, Xs, dY), G))
+
+
+@pytest.mark.parametrize("T,n_in,n_out", [(3, 64, 5), (2, 96, 3), (5, 32, 7)])
+def test_mxfp8_operand_products_brute_force(T, n_in, n_out):
+    """linear_fwd_mxfp8, linear_dgrad_mxfp8w and linear_wgrad_accum_mxfp8x equal triple loops over
+    operands decoded element by element with the scalar E4M3 and E8M0 rules."""
+    case = _mx_operands(T, n_in, n_out, seed=T * 31 + n_in + n_out)
+    assert all(_mx_matches(linear.linear_fwd_mxfp8, linear.linear_dgrad_mxfp8w,
+                           linear.linear_wgrad_accum_mxfp8x, case))
+
+
+def test_mxfp8_operand_pins_catch_planted_slips():
+    """Plausible mistakes in the three compositions each fail the brute-force comparison."""
+    deq, e4m3, e8m0 = numerics.mxfp8_dequant, numerics.e4m3_to_f64, numerics.e8m0_to_f64
+    fwd, dgrad, wgrad = linear.linear_fwd_mxfp8, linear.linear_dgrad_mxfp8w, linear.linear_wgrad_accum_mxfp8x
+    square = _mx_operands(32, 64, 32, seed=5)      # T == out: the X and W scale arrays can be swapped
+    cube = _mx_operands(3, 64, 64, seed=6)         # in == out: W and W^T have the same shape
+    slips = {
+        "fwd: X and W scales swapped": (square, lambda Xq, Xs, Wq, Ws: linear.linear_fwd(deq(Xq, Ws), deq(Wq, Xs)),
+                                        dgrad, wgrad),
+        "fwd: W scales ignored": (square, lambda Xq, Xs, Wq, Ws: linear.linear_fwd(deq(Xq, Xs), e4m3(Wq)), dgrad, wgrad),
+        "fwd: first block's scale for the whole row": (
+            square, lambda Xq, Xs, Wq, Ws: linear.linear_fwd(e4m3(Xq) * e8m0(Xs[:, :1]), deq(Wq, Ws)), dgrad, wgrad),
+        "dgrad: W transposed": (cube, fwd, lambda dY, Wq, Ws: linear.linear_dgrad(dY, deq(Wq, Ws).T), wgrad),
+        "dgrad: scale exponent off by one": (cube, fwd, lambda dY, Wq, Ws: linear.linear_dgrad(dY, deq(Wq, Ws) * 2.0),
+                                             wgrad),
+        "wgrad: main_grad dropped": (square, fwd, dgrad, lambda G0, Xq, Xs, dY: linear.linear_wgrad(deq(Xq, Xs), dY)),
+        "wgrad: X scales ignored": (square, fwd, dgrad,
+                                    lambda G0, Xq, Xs, dY: linear.linear_wgrad_accum(G0, e4m3(Xq), dY)),
+    }
+    for name, (case, f, d, w) in slips.items():
+        assert not all(_mx_matches(f, d, w, case)), name

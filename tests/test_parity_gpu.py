@@ -69,10 +69,10 @@ def test_fwd_dgrad_wgrad_elementwise(T, n_in, n_out):
 
 @pytest.mark.parametrize("cfg", range(25))
 @pytest.mark.parametrize("T,n_in,n_out", [(300, 264, 520), (1000, 2056, 264), (2111, 1032, 776), (4104, 264, 520)])
-def test_every_tile_config(monkeypatch, cfg, T, n_in, n_out):
-    """Each direct-to-LDS tile configuration, forced through SL_GEMM_CONFIG, on ragged shapes."""
+def test_every_tile_config(tune, cfg, T, n_in, n_out):
+    """Each direct-to-LDS tile configuration, forced through sl_set_tuning, on ragged shapes."""
     say(f"case cfg={cfg} T={T} in={n_in} out={n_out}")
-    monkeypatch.setenv("SL_GEMM_CONFIG", str(cfg))
+    tune(gemm=cfg)
     X, W, dY = rand_case(T, n_in, n_out, 31 + cfg)
     G0 = synth.normal_f32((n_out, n_in), 98)
     Xd, Wd, dYd = dev_bf16(X), dev_bf16(W), dev_bf16(dY)
@@ -266,6 +266,50 @@ def test_wgrad_is_deterministic():
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
+def _check_non_finite(got, ref, tol):
+    """NaN and infinity in the same places (infinities with the same sign); finite entries to tol."""
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    inf = np.isinf(ref)
+    assert np.array_equal(np.isinf(got), inf)
+    assert np.array_equal(np.sign(got[inf]), np.sign(ref[inf]))
+    fin = np.isfinite(ref)
+    assert ol.rel_err(got[fin], ref[fin]) <= tol
+    return int(np.isnan(ref).sum()), int(inf.sum())
+
+
+@pytest.mark.parametrize("T,n_in,n_out", [(300, 264, 520), (2048, 1024, 1536)])
+def test_nan_and_inf_propagate(T, n_in, n_out):
+    """NaN and +-inf in X, in dY and in the old main_grad reach exactly the outputs the definition
+    says (a NaN row of X gives a NaN row of Y and a NaN column of main_grad, ...), through the
+    unsplit and (second shape) the split-K weight gradient; the finite outputs keep parity."""
+    say(f"case non-finite T={T} in={n_in} out={n_out} ws={sl.sl_wgrad_workspace_bytes(T, n_in, n_out)}")
+    X, W, dY = rand_case(T, n_in, n_out, 61)
+    rng = np.random.default_rng(62)
+    t = rng.choice(T, 4, replace=False)
+    i = rng.choice(n_in, 4, replace=False)
+    o = rng.choice(n_out, 4, replace=False)
+    X[t[0], i[0]] = 0x7FC0                 # NaN
+    X[t[1], i[1]] = 0x7F80                 # +inf
+    dY[t[2], o[0]] = 0x7FC0                # NaN
+    dY[t[3], o[1]] = 0xFF80                # -inf
+    G0 = synth.normal_f32((n_out, n_in), 63)
+    G0[o[2], i[2]] = np.nan
+    G0[o[3], i[3]] = -np.inf
+    Xd, Wd, dYd = dev_bf16(X), dev_bf16(W), dev_bf16(dY)
+    Gd = torch.from_numpy(G0).cuda()
+    Y = sl.sl_linear_fwd(Xd, Wd)
+    dX = sl.sl_linear_dgrad(dYd, Wd)
+    sl.sl_linear_wgrad_accum(Xd, dYd, Gd)
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore"):
+        ry, rdx, rg = ol.linear_fwd(X, W), ol.linear_dgrad(dY, W), ol.linear_wgrad_accum(G0, X, dY)
+    ny = _check_non_finite(host_f64(Y), ry, TOL_BF16)
+    ndx = _check_non_finite(host_f64(dX), rdx, TOL_BF16)
+    ng = _check_non_finite(host_f64(Gd), rg, TOL_F32)
+    say(f"  (NaN, inf) counts: Y {ny} dX {ndx} main_grad {ng}")
+    assert ny[0] == n_out and ny[1] > 0 and ndx[0] == n_in and ng[0] >= n_in + n_out - 1
+
+
 def test_grad_buffer_zero_fill():
     say("case zero fill")
     for n in (1, 3, 4, 1023, 1 << 20, (1 << 20) + 5):
@@ -331,10 +375,10 @@ def test_mxfp8_elementwise(T, n_in, n_out):
 
 @pytest.mark.parametrize("cfg", range(3))
 @pytest.mark.parametrize("T,n_in,n_out", [(300, 384, 520), (1000, 512, 776), (2050, 1024, 264), (4100, 256, 3336)])
-def test_mxfp8_fwd_every_config(monkeypatch, cfg, T, n_in, n_out):
-    """Each block-scaled fp8 forward configuration, forced through SL_F8_CONFIG, on ragged M/N."""
+def test_mxfp8_fwd_every_config(tune, cfg, T, n_in, n_out):
+    """Each block-scaled fp8 forward configuration, forced through sl_set_tuning, on ragged M/N."""
     say(f"case mxfp8 fwd cfg={cfg} T={T} in={n_in} out={n_out}")
-    monkeypatch.setenv("SL_F8_CONFIG", str(cfg))
+    tune(f8=cfg)
     Xq, Xs = synth.mxfp8_normal((T, n_in), 31 + cfg)
     Wq, Ws = synth.mxfp8_normal((n_out, n_in), 32 + cfg, synth.W_STD)
     Y = sl.sl_linear_fwd_mxfp8(dev_u8(Xq), dev_u8(Xs), dev_u8(Wq), dev_u8(Ws))
@@ -448,12 +492,13 @@ def run_workload_sampled(key, mbs=None):
         weights[name] = wt
         if not w.mxfp8:
             buf.param(name).copy_(dev_bf16(wt))
-    # accumulators of the sampled reference entries
+    # sampled main_grad entries (so[j], si[j]): the oracle accumulates the [256, 256] block of
+    # main_grad over rows so and columns si, whose diagonal holds them
     samples = {}
     for name in w.step_params:
         o, i = w.params[name]
         rng = np.random.default_rng(7)
-        samples[name] = (rng.integers(0, o, 256), rng.integers(0, i, 256), np.zeros(256))
+        samples[name] = (rng.integers(0, o, 256), rng.integers(0, i, 256), np.zeros((256, 256)))
     errs = []
     for k in range(mbs):
         for name in w.step_params:
@@ -469,7 +514,7 @@ def run_workload_sampled(key, mbs=None):
                 sl.sl_linear_wgrad_accum_mxfp8x(dev_u8(Xq), dev_u8(Xs), dev_bf16(dyk), buf.main_grad(name))
                 Yr = ol.linear_fwd_mxfp8(Xq[rows], Xs[rows], Wq, Ws)
                 dXr = ol.linear_dgrad_mxfp8w(dyk[rows], Wq, Ws)
-                xf = ol.mxfp8_dequant(Xq, Xs)
+                xf = ol.mxfp8_dequant(Xq, Xs)          # the exact X the wgrad contracts with
             else:
                 Wd = buf.param(name)
                 Xd = dev_bf16(xk)
@@ -479,18 +524,17 @@ def run_workload_sampled(key, mbs=None):
                 sl.sl_linear_wgrad_accum(Xd, dYd, buf.main_grad(name))
                 Yr = ol.linear_fwd(xk[rows], weights[name])
                 dXr = ol.linear_dgrad(dyk[rows], weights[name])
-                xf = ol._f64(xk)
+                xf = xk
             torch.cuda.synchronize()
             errs.append(ol.rel_err(host_f64(Y[torch.from_numpy(rows).cuda()]), Yr))
             errs.append(ol.rel_err(host_f64(dX[torch.from_numpy(rows).cuda()]), dXr))
             so, si, acc = samples[name]
-            dyf = ol._f64(dyk)
-            acc += np.einsum("tk,tk->k", dyf[:, so], xf[:, si])
+            samples[name] = (so, si, ol.linear_wgrad_accum(acc, xf[:, si], dyk[:, so]))
             assert errs[-1] <= TOL_BF16 and errs[-2] <= TOL_BF16, (key, k, name, errs[-2:])
     for name in w.step_params:
         so, si, acc = samples[name]
         got = host_f64(buf.main_grad(name))[so, si]
-        e = ol.rel_err(got, acc)
+        e = ol.rel_err(got, np.diag(acc))
         say(f"  {key} {name} main_grad sampled rel err {e:.2e}")
         assert e <= TOL_F32
     # padding and the grad views of params outside the step stay zero
@@ -503,7 +547,10 @@ def run_workload_sampled(key, mbs=None):
     say(f"  {key} max bf16 sampled rel err {max(errs):.2e}")
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("key", ["c2", "c3", "c4", "c5"])
 def test_full_size_workload_sampled(key):
+    """Every micro-batch of the workload (8 for c2 and c5: main_grad zeroed once, then accumulated
+    over all of them with no reduction in between) in the benchmark's launch configuration."""
     say(f"case workload {key}")
-    run_workload_sampled(key, mbs=2 if key in ("c2", "c5") else None)
+    run_workload_sampled(key)
