@@ -140,6 +140,24 @@ int sl_linear_wgrad_accum(void* stream, const void* X, const void* dY, float* ma
                           void* workspace, size_t workspace_bytes);
 
 /* ---------------------------------------------------------------------------------------------
+ * The weight gradient for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc.  Same operation, arguments
+ * (other than the workspace), results and kernels as sl_linear_wgrad_accum; the split-K partial
+ * planes go into a library-owned device array of SL_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU
+ * holds from module load until the process ends.  The call allocates and frees nothing.
+ *   - A shape whose plan needs more than that (sl_wgrad_workspace_bytes(T, in, out) >
+ *     SL_NOALLOC_SCRATCH_BYTES) returns SL_EWORKSPACE and launches nothing.
+ *   - `stream` must belong to the current device (SL_EINVAL otherwise): the array is the current
+ *     device's, resolved at the first call on that device.
+ *   - Every call on one GPU shares that GPU's array, and its partial planes are written and read
+ *     within the call (nothing needs clearing between calls).  Calls that overlap on one GPU --
+ *     on different streams, or from different host threads -- race on the array: serialise them.
+ * ------------------------------------------------------------------------------------------- */
+#define SL_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int sl_linear_wgrad_accum_noalloc(void* stream, const void* X, const void* dY, float* main_grad,
+                                  int64_t T, int64_t in, int64_t out);
+
+/* ---------------------------------------------------------------------------------------------
  * MXFP8 operand variants (NVIDIA Megatron-Core guide "Generalized Tensor Parallelism",
  * section 1.3: E4M3 elements with one E8M0 scale per 32 elements).  A quantised matrix M[r, c]
  * is passed as codes Mq[r, c] (uint8, E4M3FN) and scales Ms[r, c/32] (uint8, E8M0), and stands

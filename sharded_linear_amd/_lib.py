@@ -31,6 +31,7 @@ PROTOTYPES = {
     "sl_linear_dgrad": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64]),
     "sl_wgrad_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64]),
     "sl_linear_wgrad_accum": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_sz]),
+    "sl_linear_wgrad_accum_noalloc": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64]),
     "sl_linear_fwd_mxfp8": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64]),
     "sl_mxfp8_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64]),
     "sl_linear_dgrad_mxfp8w": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_sz]),

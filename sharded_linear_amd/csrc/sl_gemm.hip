@@ -680,6 +680,59 @@ extern "C" int sl_linear_wgrad_accum(void* stream, const void* X, const void* dY
   return st ? st : reduce_splits(hs, a);
 }
 
+// ---- the weight gradient without allocation --------------------------------------------------
+// For callers that cannot allocate: the split-K partial planes live in a file-scope device array
+// instead of a caller workspace.  Each GPU holds its own copy from module load until the process
+// ends; host code reaches it only through the address hipGetSymbolAddress returns on that device
+// (the array's name in host code is a host-side stand-in, not a device address).
+
+constexpr size_t kNoAllocScratchBytes = size_t(SL_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// This device's `scratch`, resolved once per device with that device current (the stream must
+// belong to the current device).  Two threads racing on the first call both store the same
+// address.
+int device_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SL_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return SL_EINVAL;
+  hipDevice_t sdev = -1;
+  if (hipStreamGetDevice(st, &sdev) != hipSuccess) return SL_EHIP;
+  if (sdev != dev) return SL_EINVAL;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SL_EHIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return SL_OK;
+}
+
+}  // namespace
+
+extern "C" int sl_linear_wgrad_accum_noalloc(void* stream, const void* X, const void* dY, float* main_grad,
+                                             int64_t T, int64_t in, int64_t out) {
+  int st = check_dims(T, in, out, 8);
+  if (st) return st;
+  if (T == 0 || in == 0 || out == 0) return SL_OK;
+  if (!X || !dY || !main_grad) return SL_EINVAL;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(main_grad)) return SL_EALIGN;
+  const size_t need = wgrad_ws_bytes(T, in, out);
+  if (need > kNoAllocScratchBytes) return SL_EWORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (need) {
+    st = device_scratch(hs, &ws);
+    if (st) return st;
+  }
+  return sl_linear_wgrad_accum(stream, X, dY, main_grad, T, in, out, ws, need ? kNoAllocScratchBytes : 0);
+}
+
 // ---- MXFP8 operand entry points -----------------------------------------------------------
 // The native paths need 128 | in (whole 4-block scale dwords per stage) and dword-aligned scale
 // rows; other shapes take the register-staged kernels, which dequantise in registers.

@@ -142,6 +142,20 @@ def sl_linear_wgrad_accum(X: torch.Tensor, dY: torch.Tensor, main_grad: torch.Te
     return main_grad
 
 
+def sl_linear_wgrad_accum_noalloc(X: torch.Tensor, dY: torch.Tensor, main_grad: torch.Tensor) -> torch.Tensor:
+    """main_grad += dY^T . X in fp32, in place, with the split-K planes in the library's own device
+    array (no workspace, no allocation)."""
+    dev = _device(X)
+    T, n_in = X.shape
+    n_out = dY.shape[1]
+    _want(X, "X", BF16, (T, n_in), dev)
+    _want(dY, "dY", BF16, (T, n_out), dev)
+    _want(main_grad, "main_grad", F32, (n_out, n_in), dev)
+    check("sl_linear_wgrad_accum_noalloc", lib().sl_linear_wgrad_accum_noalloc(
+        _stream(dev), _ptr(X), _ptr(dY), _ptr(main_grad), T, n_in, n_out))
+    return main_grad
+
+
 def sl_linear_fwd_mxfp8(Xq, Xs, Wq, Ws, Y=None):
     """Y = deq(Xq, Xs) . deq(Wq, Ws)^T (bf16 out); codes and scales are uint8."""
     dev = _device(Xq)

@@ -244,3 +244,18 @@ def test_mxfp8x_checks_the_whole_workspace_before_launching():
     assert need > xb                                          # the planes follow the operand
     assert L.sl_linear_wgrad_accum_mxfp8x(None, A, A, A, A, T, n_in, n_out, A, xb) == SL_EWORKSPACE
     assert L.sl_linear_wgrad_accum_mxfp8x(None, A, A, A, A, T, n_in, n_out, A, need - 256) == SL_EWORKSPACE
+
+
+def test_noalloc_wgrad_validation():
+    """The no-allocation weight gradient validates like the workspace form and refuses plans whose
+    partial planes exceed its 64 MiB array, before any HIP call."""
+    f = _lib.lib().sl_linear_wgrad_accum_noalloc
+    ws = _lib.lib().sl_wgrad_workspace_bytes
+    assert f(None, A, A, A, 16, 12, 16) == SL_ESHAPE
+    assert f(None, MIS, A, A, 16, 16, 16) == SL_EALIGN
+    assert f(None, A, None, A, 16, 16, 16) == SL_EINVAL
+    assert f(None, A, A, A, -1, 16, 16) == SL_EINVAL
+    assert f(None, None, None, None, 0, 16, 16) == SL_OK
+    assert ws(8192, 4096, 1536) > 64 << 20
+    assert f(None, A, A, A, 8192, 4096, 1536) == SL_EWORKSPACE
+    assert 0 < ws(8192, 2048, 1536) <= 64 << 20 and 0 < ws(8192, 1024, 2048) <= 64 << 20   # c3's splits fit
