@@ -504,6 +504,102 @@ int run_v1(hipStream_t st, Args& a, const Plan& p) {
   return launch<128, 128, A_KMAJ, B_KMAJ, EA, EB, EPI>(st, a);
 }
 
+// ---- whole rounds plus a tail on smaller tiles -----------------------------------------------
+// A product whose 256x256 tiles make whole rounds of the 256 CUs plus a partial last round runs in
+// two launches: a region of whole rounds of 256x256 tiles (all of M and a prefix of N, or a prefix
+// of M and all of N), then the rest of the output on 256x128 tiles, which covers the tail in about
+// half a round.  Each output element is still computed by one workgroup with one k order, so the
+// result is the same as the single launch's up to that order and stays deterministic.  Only
+// unsplit products on the default 256x256 configuration are split; a forced configuration or split
+// count keeps one launch.
+struct Region {
+  int64_t m_off, n_off, M, N;
+  Plan p;
+};
+
+// relative throughput of the 256x128 tail configurations against the 256x256 one on the same work
+constexpr double kTailEff[3] = {0.85, 0.85, 0.82};   // fwd, dgrad, wgrad
+
+int plan_regions(Kind kind, const Plan& p, int64_t M, int64_t N, int64_t K, int64_t a_bytes, int64_t b_bytes,
+                 Region out[2]) {
+  out[0] = {0, 0, M, N, p};
+  if (!p.v2 || p.cfg != 21 || p.splits != 1 || config_override(kind) >= 0 || splits_override()) return 1;
+  const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256, tiles = tm * tn;
+  if (tiles < 256 || tiles % 256 == 0) return 1;
+  const int tail_cfg = kind == Kind::Wgrad ? 20 : 24;
+  const double eff = kTailEff[int(kind)];
+  auto rounds = [](int64_t t) { return double((t + 255) / 256); };
+  double best = 0.95 * rounds(tiles);
+  int n = 1;
+  // along N: the first n1 tile columns (tm x n1 a multiple of 256), the remaining columns on 256x128
+  for (int64_t n1 = tn - 1; n1 >= 1; --n1) {
+    if ((tm * n1) % 256) continue;
+    const int64_t N2 = N - n1 * 256;
+    const double cost = rounds(tm * n1) + 0.5 / eff * rounds(tm * ((N2 + 127) / 128));
+    if (cost < best) {
+      best = cost;
+      out[0] = {0, 0, M, n1 * 256, p};
+      out[1] = {0, n1 * 256, M, N2, make_plan_cfg(kind, false, M, N2, K, a_bytes, b_bytes, tail_cfg)};
+      n = 2;
+    }
+    break;
+  }
+  // along M: the first m1 tile rows, the remaining rows on 256x128
+  for (int64_t m1 = tm - 1; m1 >= 1; --m1) {
+    if ((m1 * tn) % 256) continue;
+    const int64_t M2 = M - m1 * 256;
+    const double cost = rounds(m1 * tn) + 0.5 / eff * rounds(((M2 + 255) / 256) * ((N + 127) / 128));
+    if (cost < best) {
+      best = cost;
+      out[0] = {0, 0, m1 * 256, N, p};
+      out[1] = {m1 * 256, 0, M2, N, make_plan_cfg(kind, false, M2, N, K, a_bytes, b_bytes, tail_cfg)};
+      n = 2;
+    }
+    break;
+  }
+  if (n == 2) {
+    // the tail region runs unsplit like the first; its configuration prefills a 3- or 4-stage ring,
+    // so it needs that many k stages
+    Plan& t = out[1].p;
+    t.splits = 1;
+    t.kps = int((K + t.bk - 1) / t.bk);
+    if (!t.v2 || t.kps < gemm2_min_stages(tail_cfg)) {
+      out[0] = {0, 0, M, N, p};
+      n = 1;
+    }
+  }
+  return n;
+}
+
+int run_v2(hipStream_t st, Kind kind, const Args& a, const Plan& p, int64_t a_bytes, int64_t b_bytes);
+
+// Launch a product through plan_regions: each region is the same product on sub-views of the
+// operands (a K-major operand is offset by whole rows, an MN-major one by columns) and of C.
+int run_v2_regions(hipStream_t st, Kind kind, const Args& a, const Plan& p, int64_t a_bytes, int64_t b_bytes) {
+  Region r[2];
+  const int n = plan_regions(kind, p, a.M, a.N, a.K, a_bytes, b_bytes, r);
+  if (n == 1) return run_v2(st, kind, a, p, a_bytes, b_bytes);
+  const bool a_kmaj = kind != Kind::Wgrad, b_kmaj = kind == Kind::Fwd;
+  const int64_t cbytes = kind == Kind::Wgrad ? 4 : 2;
+  for (int i = 0; i < n; ++i) {
+    Args s = a;
+    const int64_t ao = (a_kmaj ? r[i].m_off * a.a.ld : r[i].m_off) * 2;
+    const int64_t bo = (b_kmaj ? r[i].n_off * a.b.ld : r[i].n_off) * 2;
+    s.a.p = static_cast<const char*>(a.a.p) + ao;
+    s.b.p = static_cast<const char*>(a.b.p) + bo;
+    s.c = static_cast<char*>(a.c) + (r[i].m_off * a.ldc + r[i].n_off) * cbytes;
+    s.M = int(r[i].M);
+    s.N = int(r[i].N);
+    s.a.rows = int(r[i].M);
+    s.b.rows = int(r[i].N);
+    s.splits = 1;
+    s.kt_per_split = r[i].p.kps;
+    const int st_ = run_v2(st, kind, s, r[i].p, a_bytes - ao, b_bytes - bo);
+    if (st_) return st_;
+  }
+  return SL_OK;
+}
+
 int run_v2(hipStream_t st, Kind kind, const Args& a, const Plan& p, int64_t a_bytes, int64_t b_bytes) {
   Gemm2Args g{};
   g.a = a.a.p; g.b = a.b.p; g.c = a.c;
@@ -562,7 +658,7 @@ int linear_fwd(hipStream_t hs, const void* X, const void* W, float alpha, void* 
   a.c = Y;
   a.ldc = out;
   a.alpha = alpha;
-  if (p.v2) return run_v2(hs, Kind::Fwd, a, p, T * in * 2, out * in * 2);
+  if (p.v2) return run_v2_regions(hs, Kind::Fwd, a, p, T * in * 2, out * in * 2);
   return run_v1<true, true, Elem::BF16, Elem::BF16, Epi::StoreBF16>(hs, a, p);
 }
 
@@ -581,7 +677,7 @@ int linear_dgrad(hipStream_t hs, const void* dY, const void* W, float alpha, voi
   a.c = dX;
   a.ldc = in;
   a.alpha = alpha;
-  if (p.v2) return run_v2(hs, Kind::Dgrad, a, p, T * out * 2, out * in * 2);
+  if (p.v2) return run_v2_regions(hs, Kind::Dgrad, a, p, T * out * 2, out * in * 2);
   return run_v1<true, false, Elem::BF16, Elem::BF16, Epi::StoreBF16>(hs, a, p);
 }
 
@@ -675,7 +771,7 @@ extern "C" int sl_linear_wgrad_accum(void* stream, const void* X, const void* dY
   st = bind_workspace(a, p, out, in, workspace, workspace_bytes);
   if (st) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  st = p.v2 ? run_v2(hs, Kind::Wgrad, a, p, T * out * 2, T * in * 2)
+  st = p.v2 ? run_v2_regions(hs, Kind::Wgrad, a, p, T * out * 2, T * in * 2)
             : run_v1<false, false, Elem::BF16, Elem::BF16, Epi::AccumF32>(hs, a, p);
   return st ? st : reduce_splits(hs, a);
 }

@@ -88,6 +88,35 @@ def test_every_tile_config(tune, cfg, T, n_in, n_out):
     assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
 
 
+# (T, in, out) whose forward, dgrad or weight gradient has 272 or 288 tiles of 256x256: split along N
+# or along M, one shape per product and direction
+REGION_SHAPES = [(4096, 256, 4352), (4224, 512, 4096), (4096, 4352, 256), (4224, 4096, 512), (256, 4352, 4096),
+                 (320, 4096, 4480)]
+
+
+@pytest.mark.parametrize("T,n_in,n_out", REGION_SHAPES)
+def test_whole_rounds_plus_tail_regions(T, n_in, n_out):
+    """Shapes whose 256x256 tiles make one whole round plus a partial one run as two launches (whole
+    rounds of 256x256 tiles, then the rest on 256x128 tiles) -- split along N or along M, for each
+    product: element by element against the oracle, and the weight gradient stays deterministic."""
+    say(f"case regions T={T} in={n_in} out={n_out}")
+    X, W, dY = rand_case(T, n_in, n_out, 41)
+    G0 = synth.normal_f32((n_out, n_in), 42)
+    Xd, Wd, dYd = dev_bf16(X), dev_bf16(W), dev_bf16(dY)
+    Ga, Gb = torch.from_numpy(G0).cuda(), torch.from_numpy(G0).cuda()
+    Y = sl.sl_linear_fwd(Xd, Wd)
+    dX = sl.sl_linear_dgrad(dYd, Wd)
+    sl.sl_linear_wgrad_accum(Xd, dYd, Ga)
+    sl.sl_linear_wgrad_accum(Xd, dYd, Gb)
+    torch.cuda.synchronize()
+    assert torch.equal(Ga.view(torch.int32), Gb.view(torch.int32))
+    e_y = ol.rel_err(host_f64(Y), ol.linear_fwd(X, W))
+    e_dx = ol.rel_err(host_f64(dX), ol.linear_dgrad(dY, W))
+    e_g = ol.rel_err(host_f64(Ga), ol.linear_wgrad_accum(G0, X, dY))
+    say(f"  rel err Y {e_y:.2e} dX {e_dx:.2e} main_grad {e_g:.2e}")
+    assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
+
+
 def test_c1_two_microbatches_into_buffer_view():
     w = configs.WORKLOADS["c1"]
     say("case c1")
