@@ -72,6 +72,32 @@ struct F8Tile {
       }
     }
   }
+  // The code loads of load() alone (the kernels that cache their scales by groups).
+  template <int WAVES>
+  __device__ static __forceinline__ void load_codes(i32x4 rs, char* lds, int lane, int wave, int row0, int rows,
+                                                    int k0, int K, int64_t ld) {
+#pragma unroll
+    for (int it = 0; it < kLoads / WAVES; ++it) {
+      const int wl = it * WAVES + wave;
+      const int p = wl * 64 + lane;
+      const int r = p / kF8CPR, c = (p % kF8CPR) ^ swz128(p / kF8CPR);
+      const int gr = row0 + r, k = k0 + c * 16;
+      const uint32_t off = (gr < rows && k < K) ? uint32_t(int64_t(gr) * ld + k) : kOOB;
+      lds_dma16(rs, lds_addr(lds + wl * 1024), off);
+    }
+  }
+  // Scale group G: the E8M0 scales of blocks 16G .. 16G+15 (stages 4G .. 4G+3), 16 bytes per
+  // row, row r at LDS byte 16 r.  Wave-load q covers rows 64q .. 64q+63, one 16-byte lane each;
+  // the row's bytes are contiguous and 16-byte aligned in HBM when K % 512 == 0 and the scale
+  // array is 16-byte aligned.
+  static constexpr int kGroupBytes = R * 16;
+  static constexpr int kGroupLoads = R / 64;
+  __device__ static __forceinline__ void load_group(i32x4 rss, char* lds_s, int q, int lane, int row0, int rows, int G,
+                                                    int K) {
+    const int gr = row0 + q * 64 + lane, nb = K / 32, b = 16 * G;
+    const uint32_t off = (gr < rows && b < nb) ? uint32_t(int64_t(gr) * nb + b) : kOOB;
+    lds_dma16(rss, lds_addr(lds_s + q * 1024), off);
+  }
   // 32 bytes of fragment row r0 + l%32 for k64 step ks: chunks 4ks+g and 4ks+2+g
   __device__ static __forceinline__ i32x8 frag(const char* lds, int r0, int ks, int lane) {
     const int r = r0 + (lane & 31), g = lane >> 5;
@@ -88,19 +114,44 @@ struct F8Tile {
   }
 };
 
-template <int BM, int BN, int S, int WGM, int WGN, bool ACC>
+// Block scales, two ways.  SC false: each stage carries one dword of 4 scales per row, loaded
+// with the stage (a 4-byte gather per row at the scale array's row stride).  SC true: the scales
+// of four stages are loaded at once, 16 bytes per row, into a double-buffered group cache after
+// the operand ring; group G + 1 is loaded at the first stage of group G, into the buffer group
+// G - 1 has finished with, and before that stage's code loads, so the per-stage vmcnt waits
+// (which count code loads only) cover it.  That needs a quarter of the scale loads and of the
+// cache lines they touch.
+template <int BM, int BN, int S, int WGM, int WGN, bool ACC, bool SC>
+struct F8Layout {
+  using TA = F8Tile<BM>;
+  using TB = F8Tile<BN>;
+  static constexpr int WAVES = WGM * WGN;
+  // SC false, stage layout: A codes | B codes | A scale dwords | B scale dwords | 256-byte pad
+  static constexpr int kScaleOff = TA::kBytes + TB::kBytes;
+  static constexpr int kPadOff = kScaleOff + ((TA::kScaleBytes + TB::kScaleBytes + 255) / 256) * 256;
+  static constexpr int kStage = SC ? TA::kBytes + TB::kBytes : kPadOff + 256;
+  // SC true: group cache [2 buffers][A rows | B rows][16 bytes] after the S stages
+  static constexpr int kCacheOff = S * kStage;
+  static constexpr int kGroupBytes = TA::kGroupBytes + TB::kGroupBytes;
+  static constexpr int kGroupLoads = TA::kGroupLoads + TB::kGroupLoads;
+  static constexpr int kRing = kCacheOff + (SC ? 2 * kGroupBytes : 0);
+  static constexpr int kEpi = WAVES * EpiOf<BM / WGM, BN / WGN, ACC>::kBytes;
+  static constexpr int kLds = kRing > kEpi ? kRing : kEpi;
+  static_assert(kLds <= 160 * 1024, "LDS");
+  static_assert(!SC || kGroupLoads <= WAVES, "one scale wave-load per wave per group");
+};
+
+template <int BM, int BN, int S, int WGM, int WGN, bool ACC, bool SC>
 __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
+  using L = F8Layout<BM, BN, S, WGM, WGN, ACC, SC>;
   constexpr int WAVES = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN, TM = WM / 32, TN = WN / 32;
   using TA = F8Tile<BM>;
   using TB = F8Tile<BN>;
-  // stage layout: A codes | B codes | A scale dwords | B scale dwords | 256-byte pad
-  constexpr int kScaleOff = TA::kBytes + TB::kBytes;
-  constexpr int kPadOff = kScaleOff + ((TA::kScaleBytes + TB::kScaleBytes + 255) / 256) * 256;
-  constexpr int kStage = kPadOff + 256;
+  constexpr int kScaleOff = L::kScaleOff, kPadOff = L::kPadOff, kStage = L::kStage;
   static_assert(TA::kLoads % WAVES == 0 && TB::kLoads % WAVES == 0, "loads per wave");
-  constexpr int kLoadsPerWave = (TA::kLoads + TB::kLoads) / WAVES + TA::template kScaleLoadsPerWave<WAVES> +
-                                TB::template kScaleLoadsPerWave<WAVES>;
+  constexpr int kLoadsPerWave = (TA::kLoads + TB::kLoads) / WAVES +
+                                (SC ? 0 : TA::template kScaleLoadsPerWave<WAVES> + TB::template kScaleLoadsPerWave<WAVES>);
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -128,16 +179,32 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
   // texture-address queue in one burst (measured 3-5 % ahead of issuing both at the top).
   auto issue = [&](int kt, int slot) {
     char* base = smem + slot * kStage;
-    char* sbase = base + kScaleOff;
     const int k0 = kt * kF8RowBytes;
-    TA::template load<WAVES>(ra, rsa, base, sbase, base + kPadOff, lane, wave, m0, g.M, k0, g.K, g.lda);
+    if constexpr (SC) {
+      TA::template load_codes<WAVES>(ra, base, lane, wave, m0, g.M, k0, g.K, g.lda);
+    } else {
+      char* sbase = base + kScaleOff;
+      TA::template load<WAVES>(ra, rsa, base, sbase, base + kPadOff, lane, wave, m0, g.M, k0, g.K, g.lda);
+    }
   };
   auto issue_b = [&](int kt, int slot) {
     char* base = smem + slot * kStage;
-    char* sbase = base + kScaleOff;
     const int k0 = kt * kF8RowBytes;
-    TB::template load<WAVES>(rb, rsb, base + TA::kBytes, sbase + TA::kScaleBytes, base + kPadOff, lane, wave, n0, g.N,
-                             k0, g.K, g.ldb);
+    if constexpr (SC) {
+      TB::template load_codes<WAVES>(rb, base + TA::kBytes, lane, wave, n0, g.N, k0, g.K, g.ldb);
+    } else {
+      char* sbase = base + kScaleOff;
+      TB::template load<WAVES>(rb, rsb, base + TA::kBytes, sbase + TA::kScaleBytes, base + kPadOff, lane, wave, n0,
+                               g.N, k0, g.K, g.ldb);
+    }
+  };
+  // scale group G into cache buffer G % 2: wave q issues the group's wave-load q
+  auto issue_group = [&](int G) {
+    if constexpr (SC) {
+      char* cb = smem + L::kCacheOff + (G & 1) * L::kGroupBytes;
+      if (wave < TA::kGroupLoads) TA::load_group(rsa, cb, wave, lane, m0, g.M, G, g.K);
+      else if (wave < L::kGroupLoads) TB::load_group(rsb, cb + TA::kGroupBytes, wave - TA::kGroupLoads, lane, n0, g.N, G, g.K);
+    }
   };
 
   f32x16 acc[TM][TN];
@@ -148,25 +215,41 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // the scale groups of the first two groups go out before any code load
+  issue_group(kt0 / 4);
+  issue_group(kt0 / 4 + 1);
 #pragma unroll
   for (int s = 0; s < S - 1; ++s) { issue(kt0 + (s < nk ? s : nk), s); issue_b(kt0 + (s < nk ? s : nk), s); }
 
   for (int it = 0; it < nk; ++it) {
     wait_vmcnt<(S - 2) * kLoadsPerWave>();
     __syncthreads();
+    const int kt = kt0 + it;
+    if (SC && it > 0 && kt % 4 == 0) issue_group(kt / 4 + 1);
     {
       const int nxt = it + S - 1;
       issue(kt0 + (nxt < nk ? nxt : nk), nxt % S);
     }
     const char* la = smem + (it % S) * kStage;
     const char* lb = la + TA::kBytes;
-    const char* lsa = la + kScaleOff;
-    const char* lsb = lsa + TA::kScaleBytes;
     uint32_t sca[TM], scb[TN];
+    if constexpr (SC) {
+      // dword kt % 4 of each row's 16 bytes in buffer (kt / 4) % 2
+      const char* cb = smem + L::kCacheOff + ((kt / 4) & 1) * L::kGroupBytes + (kt % 4) * 4;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sca[i] = TA::scales(lsa, wm * WM + i * 32, lane);
+      for (int i = 0; i < TM; ++i)
+        sca[i] = *reinterpret_cast<const uint32_t*>(cb + (wm * WM + i * 32 + (lane & 31)) * 16);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) scb[j] = TB::scales(lsb, wn * WN + j * 32, lane);
+      for (int j = 0; j < TN; ++j)
+        scb[j] = *reinterpret_cast<const uint32_t*>(cb + TA::kGroupBytes + (wn * WN + j * 32 + (lane & 31)) * 16);
+    } else {
+      const char* lsa = la + kScaleOff;
+      const char* lsb = lsa + TA::kScaleBytes;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sca[i] = TA::scales(lsa, wm * WM + i * 32, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) scb[j] = TB::scales(lsb, wn * WN + j * 32, lane);
+    }
 #pragma unroll
     for (int ks = 0; ks < kF8RowBytes / 64; ++ks) {
       if (ks == 1) {
@@ -270,20 +353,25 @@ __global__ void mx_dequant_bf16(const uint8_t* codes, const uint8_t* scales, uin
   }
 }
 
-template <int BM, int BN, int S, int WGM, int WGN, bool ACC = false>
-int launch_f8(hipStream_t st, F8Args g) {
-  constexpr int ring = S * (F8Tile<BM>::kBytes + F8Tile<BN>::kBytes +
-                            ((F8Tile<BM>::kScaleBytes + F8Tile<BN>::kScaleBytes + 255) / 256) * 256 + 256);
-  constexpr int epi = WGM * WGN * EpiOf<BM / WGM, BN / WGN, ACC>::kBytes;
-  constexpr int lds = ring > epi ? ring : epi;
-  static_assert(lds <= 160 * 1024, "LDS");
-  auto kfn = gemm_f8fwd<BM, BN, S, WGM, WGN, ACC>;
+template <int BM, int BN, int S, int WGM, int WGN, bool ACC, bool SC>
+int launch_f8_sc(hipStream_t st, F8Args g) {
+  constexpr int lds = F8Layout<BM, BN, S, WGM, WGN, ACC, SC>::kLds;
+  auto kfn = gemm_f8fwd<BM, BN, S, WGM, WGN, ACC, SC>;
   static std::atomic<uint64_t> attr{0};
   if (smem_attr_once(reinterpret_cast<const void*>(kfn), lds, attr)) return -5;
   g.tiles_m = (g.M + BM - 1) / BM;
   g.tiles_n = (g.N + BN - 1) / BN;
   hipLaunchKernelGGL(kfn, dim3(g.tiles_m * g.tiles_n, 1, ACC ? g.splits : 1), dim3(WGM * WGN * 64), lds, st, g);
   return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// The group scale cache takes 16-byte loads from each scale row: rows of K/32 scale bytes must
+// start 16-byte aligned (K % 512 == 0, aligned arrays).
+template <int BM, int BN, int S, int WGM, int WGN, bool ACC = false>
+int launch_f8(hipStream_t st, F8Args g) {
+  const bool sc = g.K % 512 == 0 && (reinterpret_cast<uintptr_t>(g.sa) & 15u) == 0 &&
+                  (reinterpret_cast<uintptr_t>(g.sb) & 15u) == 0;
+  return sc ? launch_f8_sc<BM, BN, S, WGM, WGN, ACC, true>(st, g) : launch_f8_sc<BM, BN, S, WGM, WGN, ACC, false>(st, g);
 }
 
 }  // namespace sl2

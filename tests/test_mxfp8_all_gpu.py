@@ -196,6 +196,40 @@ def test_every_fp8_tile_config(tune, cfg):
     assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
 
 
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("T,n_in,n_out", [(2560, 1536, 1024), (2560, 2048, 896)])
+def test_fp8_scale_groups(tune, cfg, T, n_in, n_out):
+    """Contractions whose length is a multiple of 512 load their block scales four stages at a time
+    into a double-buffered cache.  Each configuration, forced: the forward, the dgrad (its K = out is a
+    multiple of 512 in the first shape only) and a weight gradient in two K splits of 10 stages, so
+    the second split starts in the middle of a four-stage group; element by element."""
+    say(f"case fp8 scale groups cfg={cfg} T={T} in={n_in} out={n_out}")
+    tune(f8=cfg)
+    assert sl.sl_mxfp8_wgrad_workspace_bytes(T, n_in, n_out) == 2 * n_out * n_in * 4
+    X, W, dY = _quantised_case(T, n_in, n_out, 61 + cfg)
+    Xf, Wf, dYf = (numerics.bf16_bits_to_f64(a) for a in (X, W, dY))
+    Xq, Xs, XqT, XsT = sl.sl_mxfp8_quantize(dev_bf16(X))
+    Wq, Ws, WqT, WsT = sl.sl_mxfp8_quantize(dev_bf16(W))
+    dYq, dYs, dYqT, dYsT = sl.sl_mxfp8_quantize(dev_bf16(dY))
+    G0 = synth.normal_f32((n_out, n_in), 7)
+    G = torch.from_numpy(G0).cuda()
+    Y = sl.sl_linear_fwd_mxfp8(Xq, Xs, Wq, Ws)
+    dX = sl.sl_linear_dgrad_mxfp8(dYq, dYs, WqT, WsT)
+    sl.sl_linear_wgrad_accum_mxfp8(dYqT, dYsT, XqT, XsT, G)
+    torch.cuda.synchronize()
+    q, s_ = numerics.mx_quantize(Xf)
+    wq, ws = numerics.mx_quantize(Wf)
+    e_y = ol.rel_err(host_f64(Y), ol.linear_fwd_mxfp8(q, s_, wq, ws))
+    dq, ds = numerics.mx_quantize(dYf)
+    wqt, wst = numerics.mx_quantize_cols(Wf)
+    e_dx = ol.rel_err(host_f64(dX), ol.linear_dgrad_mxfp8(dq, ds, wqt, wst))
+    qd, sd = numerics.mx_quantize_cols(dYf)
+    qx, sx = numerics.mx_quantize_cols(Xf)
+    e_g = ol.rel_err(host_f64(G), ol.linear_wgrad_accum_mxfp8(G0, qd, sd, qx, sx))
+    say(f"  rel err Y {e_y:.2e} dX {e_dx:.2e} main_grad {e_g:.2e}")
+    assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
+
+
 @pytest.mark.parametrize("T,n_in,n_out", [(2048, 1032, 776), (4096, 4096, 2048), (2048, 4096, 4096)])
 def test_fp8_wgrad_is_deterministic(T, n_in, n_out):
     """The same weight gradient accumulated twice from the same main_grad gives the same bits:
