@@ -52,7 +52,9 @@ const char* sl_status_str(int status);
  * Tuning knobs, for measurement and tests (not needed for correct use).  sl_set_tuning forces
  * one choice for every later call and workspace query of this process; value -1 restores the
  * built-in choice.  The previous value is stored in *previous when it is not NULL.  Ranges:
- *   SL_TUNE_{FWD,DGRAD,WGRAD}_CONFIG  bf16 tile configuration 0..24 of that product
+ *   SL_TUNE_FWD_CONFIG                bf16 tile configuration 0..25 of the forward (25: 256x192
+ *                                     tiles, which only the forward has)
+ *   SL_TUNE_{DGRAD,WGRAD}_CONFIG      bf16 tile configuration 0..24 of that product
  *   SL_TUNE_SPLITK                    split count 1..64 of the bf16 weight gradient
  *   SL_TUNE_F8_CONFIG                 block-scaled fp8 configuration 0..2 (0: 256x256, 1: 128x128,
  *                                     2: 256x128), for the weight gradient as well

@@ -22,14 +22,20 @@ namespace sl2 {
 // predicate per chunk.  bf16 results stage the whole wave tile at once; fp32 results go 32 rows
 // at a time, with the old main_grad values of the next 32 rows loaded while the current ones
 // are staged (or, for wide wave tiles, the current rows' values loaded before their staging).
+//
+// A row of 6 chunks (48-column bf16 wave tiles) has no whole number of rows per 64 lanes: its
+// read-back walks the wave tile's chunks in order instead, and its swizzle flips only bit 0,
+// which keeps every chunk index inside the row.
 template <int WN, int ROWS, bool ACC>
 struct Epi {
   static constexpr int kES = ACC ? 4 : 2;               // bytes per element
   static constexpr int kRowBytes = WN * kES;
   static constexpr int kCPR = kRowBytes / 16;           // 16-byte chunks per row
-  static constexpr int kRPI = 64 / kCPR;                // rows per wave instruction
+  static constexpr bool kWhole = 64 % kCPR == 0;        // a wave instruction reads whole rows
+  static constexpr int kRPI = kWhole ? 64 / kCPR : 0;   // rows per wave instruction
+  static constexpr int kSwz = (kCPR & -kCPR) - 1;       // swizzle bits: kCPR is a multiple of kSwz + 1
   static constexpr int kBytes = ROWS * kRowBytes;       // LDS per wave
-  __device__ static __forceinline__ int off(int r, int c) { return r * kRowBytes + ((c ^ (r & (kCPR - 1))) << 4); }
+  __device__ static __forceinline__ int off(int r, int c) { return r * kRowBytes + ((c ^ (r & kSwz)) << 4); }
 };
 template <int WM, int WN, bool ACC>
 using EpiOf = Epi<WN, ACC ? 32 : WM, ACC>;
@@ -38,6 +44,7 @@ template <int WM, int WN, int TM, int TN, bool ACC, class G>
 __device__ __forceinline__ void store_tile(const G& g, f32x16 (&acc)[TM][TN], char* smem, int mw, int nw,
                                            int split, int lane, int wave) {
   using E = EpiOf<WM, WN, ACC>;
+  static_assert(E::kWhole, "32x32 blocks give wave tiles of whole-row chunks");
   char* ep = smem + wave * E::kBytes;
   const int rl = lane & 31, hl = lane >> 5;
   const int rr = lane / E::kCPR, cr = lane % E::kCPR;    // read-back: row within an instruction, chunk
@@ -132,13 +139,25 @@ __device__ __forceinline__ void store_tile16(const G& g, f32x4v (&acc)[TM][TN], 
         *reinterpret_cast<bf16x4*>(ep + E::off(i * 16 + rl, 2 * j + (gl >> 1)) + 8 * (gl & 1)) = v;
       }
     __bf16* C = static_cast<__bf16*>(g.c);
+    if constexpr (E::kWhole) {
 #pragma unroll
-    for (int t = 0; t < WM / E::kRPI; ++t) {
-      const int r = t * E::kRPI + rr, m = mw + r;
-      const uint4 v = *reinterpret_cast<const uint4*>(ep + E::off(r, cr));
-      if (m < g.M && n < g.N) *reinterpret_cast<uint4*>(C + int64_t(m) * g.ldc + n) = v;
+      for (int t = 0; t < WM / E::kRPI; ++t) {
+        const int r = t * E::kRPI + rr, m = mw + r;
+        const uint4 v = *reinterpret_cast<const uint4*>(ep + E::off(r, cr));
+        if (m < g.M && n < g.N) *reinterpret_cast<uint4*>(C + int64_t(m) * g.ldc + n) = v;
+      }
+    } else {
+      // chunk x = 64 t + lane of the wave tile, row-major: row x / kCPR, chunk x % kCPR
+      static_assert(WM * E::kCPR % 64 == 0, "the wave tile's chunks fill whole wave instructions");
+#pragma unroll
+      for (int t = 0; t < WM * E::kCPR / 64; ++t) {
+        const int x = t * 64 + lane, r = x / E::kCPR, c = x % E::kCPR, m = mw + r, nc = nw + c * 8;
+        const uint4 v = *reinterpret_cast<const uint4*>(ep + E::off(r, c));
+        if (m < g.M && nc < g.N) *reinterpret_cast<uint4*>(C + int64_t(m) * g.ldc + nc) = v;
+      }
     }
   } else {
+    static_assert(E::kWhole, "fp32 wave tiles of whole-row chunks");
     static_assert(TM % 2 == 0, "two 16-row blocks per round");
     constexpr int RI = 32 / E::kRPI;
     const bool direct = g.splits == 1;

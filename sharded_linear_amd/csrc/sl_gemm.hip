@@ -400,14 +400,17 @@ int splits_override() {
 // Tile configuration for a forward / dgrad GEMM: each candidate's time is estimated as the number
 // of rounds of workgroups over the 256 CUs times one round's work (tile area x workgroups per CU)
 // over the candidate's measured efficiency relative to the 8-wave 256x256 kernel.  The weight
-// gradient always takes 256x256 tiles and fills the chip by splitting K instead.
-int pick_config(int64_t M, int64_t N) {
+// gradient always takes 256x256 tiles and fills the chip by splitting K instead.  The forward also
+// considers the fixed-order 256x192 kernel (cfg 25).
+int pick_config(Kind kind, int64_t M, int64_t N) {
   struct Cand { int cfg, bm, bn, occ; double eff; };
   static const Cand cand[] = {{10, 256, 256, 1, 1.0}, {12, 256, 128, 2, 0.85}, {13, 128, 256, 2, 0.85},
-                              {3, 256, 128, 1, 0.78}, {4, 128, 256, 1, 0.78}, {2, 128, 128, 1, 0.6}};
+                              {3, 256, 128, 1, 0.78}, {4, 128, 256, 1, 0.78}, {2, 128, 128, 1, 0.6},
+                              {kGemm2FwdOnlyConfig, 256, 192, 1, 0.92}};
   int best = 10;
   double best_t = 0.0;
   for (const Cand& c : cand) {
+    if (c.cfg == kGemm2FwdOnlyConfig && kind != Kind::Fwd) continue;
     const int64_t rounds = (ntiles(M, N, c.bm, c.bn) + 256 * c.occ - 1) / (256 * c.occ);
     const double t = double(rounds) * double(c.bm * c.bn * c.occ) / c.eff;
     if (best_t == 0.0 || t < best_t) { best = c.cfg; best_t = t; }
@@ -447,7 +450,7 @@ Plan make_plan_cfg(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64
 Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a_bytes, int64_t b_bytes) {
   int cfg = config_override(kind);
   if (cfg < 0) {
-    cfg = kind == Kind::Wgrad ? 10 : pick_config(M, N);
+    cfg = kind == Kind::Wgrad ? 10 : pick_config(kind, M, N);
     // 256x256 tiles: the fixed-order 8-wave kernel on the 16x16x32 instruction (2 stages of 64 k)
     // for all three products.  Against the 32x32x16 kernels (fwd: 8 waves, 2 x 64 k; dgrad and
     // wgrad: 4 waves, 4 x 32 k) it measured 2-9 % ahead on the forward and up to 18 % on the
@@ -684,7 +687,8 @@ int linear_dgrad(hipStream_t hs, const void* dY, const void* W, float alpha, voi
 }  // namespace
 
 extern "C" int sl_set_tuning(int32_t knob, int32_t value, int32_t* previous) {
-  static const int hi[SL_TUNE_COUNT] = {kGemm2Configs - 1, kGemm2Configs - 1, kGemm2Configs - 1, 64, 2};
+  static const int hi[SL_TUNE_COUNT] = {kGemm2Configs - 1, kGemm2FwdOnlyConfig - 1, kGemm2FwdOnlyConfig - 1, 64, 2};
+  static_assert(kGemm2FwdOnlyConfig == kGemm2Configs - 1, "the forward-only configuration comes last");
   static const int lo[SL_TUNE_COUNT] = {0, 0, 0, 1, 0};
   if (knob < 0 || knob >= SL_TUNE_COUNT) return SL_EINVAL;
   if (value != -1 && (value < lo[knob] || value > hi[knob])) return SL_EINVAL;

@@ -18,7 +18,8 @@ struct Gemm2Args {
   float alpha = 1.0f;   // bf16 results are alpha * (A . B^T), scaled in fp32 before rounding
 };
 
-constexpr int kGemm2Configs = 25;
+constexpr int kGemm2Configs = 26;
+constexpr int kGemm2FwdOnlyConfig = 25;   // 256x192 tiles: forward only
 
 // A K-major (k contiguous) and B K-major: forward.
 int gemm2_fwd(hipStream_t st, Gemm2Args g);

@@ -497,7 +497,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
   // and loads issued a step later than that no longer land before the barrier that waits for them.
   constexpr bool ONE = MF == 16;
   constexpr int NR = TM + TN, LH = LPS / 2;
-  static_assert(LPS % 2 == 0, "loads split over two steps");
+  static_assert(ONE || LPS % 2 == 0, "loads split over two steps");
   auto memop = [&](auto ic_m, auto ic_nx, auto ic_ks, auto ic_l0, uint32_t rbase, bool loads, int kt, int slot,
                    bool ragged) {
     constexpr int m = decltype(ic_m)::value, nx = decltype(ic_nx)::value, l0 = decltype(ic_l0)::value;
@@ -636,6 +636,14 @@ int launch_g4(hipStream_t st, Gemm2Args g) {
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
+// 256x192 tiles exist for the forward only: an MN-major operand 192 wide has 24 chunks per LDS row,
+// beyond what the transposing-read swizzle keeps inside a row.
+template <bool A_KM, bool B_KM, bool ACC>
+int launch_g4_192(hipStream_t st, Gemm2Args g) {
+  if constexpr (A_KM && B_KM && !ACC) return launch_g4<2, 2, 4, A_KM, B_KM, ACC, 64, 192, 16>(st, g);
+  else return -1;
+}
+
 }  // namespace sl2
 
 // ---- dispatch ------------------------------------------------------------------------------
@@ -663,6 +671,8 @@ int launch_g4(hipStream_t st, Gemm2Args g) {
 //  20: 256x128, BK 32, 4 stages, 4 waves (128x64 wave tiles), fixed issue order         LDS  96 KiB
 //  21-23: as 17-19 with v_mfma_f32_16x16x32_bf16 (16x16 blocks, k32 steps)
 //  24: 256x128, BK 64, 3 stages, 8 waves 4x2 (64x64 wave tiles), fixed issue order, 16x16x32  LDS 144 KiB
+//  25: 256x192, BK 64, 2 stages, 8 waves 2x4 (128x48 wave tiles), fixed issue order, 16x16x32, forward
+//      only                                                                                   LDS 112 KiB
 #define SL2_DISPATCH(AK, BKM, ACC)                                                                 \
   switch (g.cfg) {                                                                                 \
     case 0: return sl2::launch_cfg<256, 256, 32, 4, 2, 2, AK, BKM, ACC>(st, g);                   \
@@ -690,6 +700,7 @@ int launch_g4(hipStream_t st, Gemm2Args g) {
     case 22: return sl2::launch_g4<2, 2, 2, AK, BKM, ACC, 64, 256, 16>(st, g);                     \
     case 23: return sl2::launch_g4<3, 2, 2, AK, BKM, ACC, 64, 128, 16>(st, g);                     \
     case 24: return sl2::launch_g4<3, 4, 2, AK, BKM, ACC, 64, 128, 16>(st, g);                     \
+    case 25: return sl2::launch_g4_192<AK, BKM, ACC>(st, g);                                       \
     default: return -1;                                                                            \
   }
 
@@ -708,7 +719,7 @@ int gemm2_wgrad(hipStream_t st, Gemm2Args g) { SL2_DISPATCH(false, false, true) 
 #if !defined(SL2_PART) || SL2_PART == 1
 
 int gemm2_min_stages(int cfg) {
-  return cfg == 15 || cfg == 16 || cfg == 20 ? 4 : cfg == 17 || cfg == 18 || cfg == 21 || cfg == 22 ? 2
+  return cfg == 15 || cfg == 16 || cfg == 20 ? 4 : cfg == 17 || cfg == 18 || cfg == 21 || cfg == 22 || cfg == 25 ? 2
          : cfg == 19 || cfg == 23 || cfg == 24 ? 3 : 1;
 }
 
@@ -718,7 +729,7 @@ void gemm2_tile(int cfg, int* bm, int* bn, int* bk) {
       {256, 256}, {256, 256}, {128, 128}, {256, 128}, {128, 256}, {256, 256}, {256, 256},
       {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {128, 256},
       {256, 128}, {256, 256}, {256, 256}, {256, 256}, {256, 256}, {256, 128}, {256, 128},
-      {256, 256}, {256, 256}, {256, 128}, {256, 128}};
+      {256, 256}, {256, 256}, {256, 128}, {256, 128}, {256, 192}};
   *bm = t[cfg][0];
   *bn = t[cfg][1];
 }

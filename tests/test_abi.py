@@ -216,7 +216,10 @@ def test_tuning_knobs_and_workspace_query_agree():
         assert ws(T, n_in, n_out) == default
         # validation: knob range and value ranges; a refused call changes nothing
         assert L.sl_set_tuning(5, 0, None) == SL_EINVAL and L.sl_set_tuning(-1, 0, None) == SL_EINVAL
-        assert L.sl_set_tuning(0, 25, None) == SL_EINVAL and L.sl_set_tuning(3, 0, None) == SL_EINVAL
+        assert L.sl_set_tuning(0, 26, None) == SL_EINVAL and L.sl_set_tuning(3, 0, None) == SL_EINVAL
+        # the 256x192 configuration is the forward's only
+        assert L.sl_set_tuning(1, 25, None) == SL_EINVAL and L.sl_set_tuning(2, 25, None) == SL_EINVAL
+        assert L.sl_set_tuning(0, 25, None) == SL_OK and L.sl_set_tuning(0, -1, None) == SL_OK
         assert L.sl_set_tuning(3, 65, None) == SL_EINVAL and L.sl_set_tuning(4, 3, None) == SL_EINVAL
         assert L.sl_set_tuning(4, -2, None) == SL_EINVAL
         assert ws(T, n_in, n_out) == default

@@ -88,6 +88,21 @@ def test_every_tile_config(tune, cfg, T, n_in, n_out):
     assert e_y <= TOL_BF16 and e_dx <= TOL_BF16 and e_g <= TOL_F32
 
 
+@pytest.mark.parametrize("T,n_in,n_out", [(300, 264, 520), (1000, 2056, 264), (2111, 1032, 776), (4104, 264, 520),
+                                          (520, 4104, 1544), (1024, 2048, 1536)])
+def test_forward_256x192_tiles(tune, T, n_in, n_out):
+    """The forward-only 256x192 configuration (cfg 25), forced, on ragged shapes: N not a multiple of
+    192, the last k stage partial, M edges inside a tile; element by element against the oracle."""
+    say(f"case fwd cfg=25 T={T} in={n_in} out={n_out}")
+    tune(fwd=25)
+    X, W, _ = rand_case(T, n_in, n_out, 51)
+    Y = sl.sl_linear_fwd(dev_bf16(X), dev_bf16(W))
+    torch.cuda.synchronize()
+    e_y = ol.rel_err(host_f64(Y), ol.linear_fwd(X, W))
+    say(f"  rel err Y {e_y:.2e}")
+    assert e_y <= TOL_BF16
+
+
 # (T, in, out) whose forward, dgrad or weight gradient has 272 or 288 tiles of 256x256: split along N
 # or along M, one shape per product and direction
 REGION_SHAPES = [(4096, 256, 4352), (4224, 512, 4096), (4096, 4352, 256), (4224, 4096, 512), (256, 4352, 4096),
