@@ -11,10 +11,12 @@
 //    row m in group g multiplies the 32-element block g of that row.  So each lane loads the two
 //    16-byte chunks 16g and 32+16g of the k step and the scale of block (k0/32 + g).
 //    Codes travel HBM->LDS directly (buffer_load ... lds, rows of 128 bytes, swizzled like the
-//    bf16 tiles); each stage also carries one dword of 4 block scales per row.  In the
-//    fp32-accumulating form the MFMAs take the B fragment (with its scales) first, so the
-//    accumulators hold C^T blocks as in the bf16 kernels and the read-modify-write of main_grad
-//    goes through the same LDS-staged epilogue (16-byte row accesses).
+//    bf16 tiles); block scales come with each stage (one dword of 4 per row) or, where K % 512 ==
+//    0, four stages at a time into a scale cache.  The MFMAs take the B fragment (with its
+//    scales) first, so the accumulators hold C^T blocks as in the bf16 kernels, and both the bf16
+//    result and the fp32 read-modify-write of main_grad go through the same LDS-staged epilogue
+//    (16-byte row accesses; for the bf16 result 1 % ahead on the all-MXFP8 step of direct
+//    two-byte stores from the accumulator layout).
 //  * dgrad / wgrad see the MXFP8 operand blocked along their N, not K; it is dequantised
 //    exactly into a bf16 workspace by mx_dequant_bf16 (an E4M3 value times a power of two has
 //    at most 4 significant bits) and the bf16 GEMM kernels run on it.
@@ -266,44 +268,13 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          if constexpr (ACC)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fb[j], fa[i], acc[i][j], 0, 0, 0, int((scb[j] >> sh) & 0xFFu), 0, int((sca[i] >> sh) & 0xFFu));
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fa[i], fb[j], acc[i][j], 0, 0, 0, int((sca[i] >> sh) & 0xFFu), 0, int((scb[j] >> sh) & 0xFFu));
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fb[j], fa[i], acc[i][j], 0, 0, 0, int((scb[j] >> sh) & 0xFFu), 0, int((sca[i] >> sh) & 0xFFu));
     }
   }
   wait_vmcnt<0>();
-  if constexpr (ACC) {
-    __syncthreads();    // every wave is past its last operand read: the stage ring becomes epilogue space
-    store_tile<WM, WN, TM, TN, ACC>(g, acc, smem, m0 + wm * WM, n0 + wn * WN, split, lane, wave);
-    return;
-  }
-  // bf16 result (A fragment first: lane l holds column l%32 of each block, rows
-  // 8(r/4) + 4(l/32) + r%4): each store instruction covers 64 contiguous bytes of two rows, which
-  // measured ahead of staging the tile through LDS here.
-  const int rib = 4 * (lane >> 5), cib = lane & 31;
-  const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
-  __bf16* C = static_cast<__bf16*>(g.c);
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * WN + j * 32 + cib;
-      const int mb = m0 + wm * WM + i * 32 + rib;
-      if (interior) {
-        __bf16* p = C + int64_t(mb) * g.ldc + n;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[int64_t(8 * (r >> 2) + (r & 3)) * g.ldc] = static_cast<__bf16>(acc[i][j][r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mb + 8 * (r >> 2) + (r & 3);
-          if (m < g.M && n < g.N) C[int64_t(m) * g.ldc + n] = static_cast<__bf16>(acc[i][j][r]);
-        }
-      }
-    }
+  __syncthreads();    // every wave is past its last operand read: the stage ring becomes epilogue space
+  store_tile<WM, WN, TM, TN, ACC>(g, acc, smem, m0 + wm * WM, n0 + wn * WN, split, lane, wave);
 }
 
 
