@@ -140,7 +140,7 @@ struct F8Layout {
   static constexpr int kEpi = WAVES * EpiOf<BM / WGM, BN / WGN, ACC>::kBytes;
   static constexpr int kLds = kRing > kEpi ? kRing : kEpi;
   static_assert(kLds <= 160 * 1024, "LDS");
-  static_assert(!SC || kGroupLoads <= WAVES, "one scale wave-load per wave per group");
+  static_assert(!SC || kGroupLoads % WAVES == 0 || kGroupLoads < WAVES, "scale wave-loads spread evenly");
 };
 
 template <int BM, int BN, int S, int WGM, int WGN, bool ACC, bool SC>
@@ -200,12 +200,16 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
                                g.N, k0, g.K, g.ldb);
     }
   };
-  // scale group G into cache buffer G % 2: wave q issues the group's wave-load q
+  // scale group G into cache buffer G % 2: wave w issues the group's wave-loads w, w + WAVES, ...
   auto issue_group = [&](int G) {
     if constexpr (SC) {
       char* cb = smem + L::kCacheOff + (G & 1) * L::kGroupBytes;
-      if (wave < TA::kGroupLoads) TA::load_group(rsa, cb, wave, lane, m0, g.M, G, g.K);
-      else if (wave < L::kGroupLoads) TB::load_group(rsb, cb + TA::kGroupBytes, wave - TA::kGroupLoads, lane, n0, g.N, G, g.K);
+#pragma unroll
+      for (int q0 = 0; q0 < L::kGroupLoads; q0 += WAVES) {
+        const int q = q0 + wave;
+        if (q < TA::kGroupLoads) TA::load_group(rsa, cb, q, lane, m0, g.M, G, g.K);
+        else if (q < L::kGroupLoads) TB::load_group(rsb, cb + TA::kGroupBytes, q - TA::kGroupLoads, lane, n0, g.N, G, g.K);
+      }
     }
   };
 
