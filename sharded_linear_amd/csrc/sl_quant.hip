@@ -53,19 +53,17 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4q __attribute__((ext_vector_type(4)));
 
 // Largest magnitude field of N words of two bf16 elements: |bf16| orders like its 15-bit magnitude.
+// Both halves are compared at once (packed 16-bit max).
 template <int N>
 __device__ __forceinline__ uint32_t mag_max(const uint32_t (&w)[N]) {
-  uint32_t m2 = 0;
+  u16x2 m = {0, 0};
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const uint32_t a = w[i] & 0x7FFF7FFFu;
-    const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
-    const uint32_t mlo = m2 & 0xFFFFu, mhi = m2 >> 16;
-    m2 = (lo > mlo ? lo : mlo) | ((hi > mhi ? hi : mhi) << 16);
-  }
-  return (m2 & 0xFFFFu) > (m2 >> 16) ? (m2 & 0xFFFFu) : (m2 >> 16);
+  for (int i = 0; i < N; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+  return m[0] > m[1] ? m[0] : m[1];
 }
 
 // Encodes N words of two bf16 elements (element 2i in the low half of word i) of a block whose
@@ -122,7 +120,9 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t m) {
 }
 
 constexpr int kQT = 128;                 // tile edge
-constexpr int kQStride = kQT + 8;        // LDS row stride (bf16 elements)
+// LDS row stride (bf16 elements): 288 bytes, so the 4 rows x 4 column quads that one 16-lane group
+// of a transposing read touches fall in distinct banks
+constexpr int kQStride = kQT + 16;
 
 template <bool ROWS, bool COLS>
 __global__ void __launch_bounds__(256) mx_quant_tile(const uint16_t* x, int64_t R, int64_t C, uint8_t* qr, uint8_t* sr,
@@ -164,12 +164,25 @@ __global__ void __launch_bounds__(256) mx_quant_tile(const uint16_t* x, int64_t 
     uint32_t q[2][8], s[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int idx = t + 256 * h, col = idx & (kQT - 1), rb = idx >> 7;
+      const int idx = t + 256 * h, rb = idx >> 7;
+      // Thread idx holds column idx % 128 (a wave: 64 adjacent columns), rows 32 rb .. 32 rb + 31.
+      // ds_read_b64_tr_b16 transposes 4 x 4 blocks of 16-bit values within each 16-lane group:
+      // source lane 4j + q reads 4 adjacent columns (quad q of the group's 16) of row j, and result
+      // lane 4q + e receives element e of those four rows -- its own column, 4 adjacent rows,
+      // packed two to a word as v expects.  Eight reads cover the 32-row block.
+      const int s16 = t & 15, jr = s16 >> 2, qc4 = s16 & 3;
+      const int col4 = ((idx & (kQT - 1)) & ~15) + 4 * qc4;
+      const uint32_t a0 = uint32_t(reinterpret_cast<uintptr_t>(
+          (const __attribute__((address_space(3))) uint16_t*)(tile + (rb * 32 + jr) * kQStride + col4)));
       uint32_t v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        v[i] = uint32_t(tile[(rb * 32 + 2 * i) * kQStride + col]) |
-               (uint32_t(tile[(rb * 32 + 2 * i + 1) * kQStride + col]) << 16);
+      for (int r4 = 0; r4 < 8; ++r4) {
+        const i16x4q x4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4q*)(uintptr_t)(a0 + r4 * 4 * kQStride * 2));
+        const uint2 p = __builtin_bit_cast(uint2, x4);
+        v[2 * r4] = p.x;
+        v[2 * r4 + 1] = p.y;
+      }
       s[h] = mx_block(v, q[h]);                  // blocks past the edges are encoded and never stored
     }
     __syncthreads();
