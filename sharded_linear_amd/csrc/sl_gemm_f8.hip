@@ -140,7 +140,6 @@ struct F8Layout {
   static constexpr int kEpi = WAVES * EpiOf<BM / WGM, BN / WGN, ACC>::kBytes;
   static constexpr int kLds = kRing > kEpi ? kRing : kEpi;
   static_assert(kLds <= 160 * 1024, "LDS");
-  static_assert(!SC || kGroupLoads % WAVES == 0 || kGroupLoads < WAVES, "scale wave-loads spread evenly");
 };
 
 template <int BM, int BN, int S, int WGM, int WGN, bool ACC, bool SC>
