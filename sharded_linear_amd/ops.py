@@ -57,7 +57,8 @@ def sl_set_tuning(knob: str, value: int) -> int:
 @contextlib.contextmanager
 def tuning(**knobs):
     """Within the block, force the given knobs (names of TUNE_KNOBS; ``gemm=n`` sets the tile
-    configuration of all three bf16 products); the previous values come back on exit."""
+    configuration of all three bf16 products, so it takes 0..24; the forward-only 256x192
+    configuration 25 is forced with ``fwd=25``); the previous values come back on exit."""
     if "gemm" in knobs:
         cfg = knobs.pop("gemm")
         knobs = {"fwd": cfg, "dgrad": cfg, "wgrad": cfg, **knobs}
