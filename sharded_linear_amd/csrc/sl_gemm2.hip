@@ -413,6 +413,15 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
   const int nkt = (g.K + BK - 1) / BK;
   const int kt0 = split * g.kt_per_split;
   const int nk = min(nkt, kt0 + g.kt_per_split) - kt0;
+  // The k tiles are walked from a starting point that depends on the XCD (blocks are dealt to
+  // the XCDs round-robin): stage j of this split (0 <= j < nk) is k tile kmap(j), a rotation by
+  // an eighth of the split per XCD.  Without it every workgroup of the chip loads the same k
+  // column of its rows at the same time; with rows a power of two apart in HBM (K = 2048 or 8192
+  // bf16), those loads pile onto the same memory channels.  The workgroups of one XCD keep one
+  // phase, so the operand panels they share in that XCD's L2 are still loaded once.  Each tile
+  // keeps one fixed k order, so results stay deterministic.
+  const int rot = ((int(blockIdx.x) % kXCD) * nk) / kXCD;
+  auto kmap = [&](int j) { const int x = j + rot; return kt0 + (x >= nk ? x - nk : x); };
 
   const i32x4 ra = rsrc(g.a, g.a_bytes), rb = rsrc(g.b, g.b_bytes);
   // load offsets relative to a stage's first k; the ragged last stage (K % 32 != 0) uses a copy
@@ -539,9 +548,9 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
     // S - 2 whole stages s + 2 .. s + S - 1.
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const bool rag = kt0 + s == nkt - 1;
-      if (ONE || s < S - 1) static_for<LPS>([&](auto lc) { load_one(lc, kt0 + s, s, rag); });
-      else static_for<LH>([&](auto lc) { load_one(lc, kt0 + s, s, rag); });
+      const bool rag = kmap(s) == nkt - 1;
+      if (ONE || s < S - 1) static_for<LPS>([&](auto lc) { load_one(lc, kmap(s), s, rag); });
+      else static_for<LH>([&](auto lc) { load_one(lc, kmap(s), s, rag); });
     }
     // stage 0 is complete once at most the later prologue stages' loads (S - 1 of them, the last
     // one only half issued unless ONE) are outstanding
@@ -567,7 +576,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
       static_for<NPS_ - 1>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         constexpr bool ld = !ONE && LDA && t == 0;
-        const int kt = kt0 + s + S - 1, lslot = (s + S - 1) % S;
+        const int kt = kmap(s + S - 1), lslot = (s + S - 1) % S;
         const bool rag = kt == nkt - 1;
         step(ic<t % 2>{}, ic<ld ? NR + LH : NR>{},
              [&](auto ic_m) { memop(ic_m, ic<(t + 1) % 2>{}, ic<t + 1>{}, ic<LH>{}, cur, ld, kt, lslot, rag); });
@@ -578,7 +587,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t nxt = lds0 + ((s + 1) % S) * kStage;
-        const int kt = kt0 + s + S;
+        const int kt = kmap(s + S);
         const bool rag = kt == nkt - 1;
         step(ic<1>{}, ic<LDB ? NR + (ONE ? LPS : LH) : NR>{},
              [&](auto ic_m) { memop(ic_m, ic<0>{}, ic<0>{}, ic<0>{}, nxt, LDB, kt, slot, rag); });
