@@ -164,16 +164,19 @@ struct OpSel<false, R, BK, SW> { using T = MNMaj<R, BK, SW>; };
 
 // Workgroup -> macro-tile: blocks are dealt round-robin to the XCDs, so the block id is first
 // remapped to make each XCD's blocks a contiguous run of tile ids; tile ids then walk groups of
-// 8 tile rows column by column, so the tiles one XCD runs at a time share A and B panels in its L2.
-template <int BM, int BN>
+// GR tile rows column by column, so the tiles one XCD runs at a time share A and B panels in its
+// L2.  GR is 8, or 4 for the dgrad kernels (there measured 3.6 % faster on c2's shapes: an XCD's
+// 32 tiles then take 4 rows of dY panels, which no other XCD of the round reads, and 8 columns
+// of W panels).
+template <int BM, int BN, int GR = 8>
 __device__ __forceinline__ void tile_origin(const Gemm2Args& g, int& m0, int& n0) {
   const int ntiles = g.tiles_m * g.tiles_n;
   const int t = xcd_remap(blockIdx.x, ntiles);
-  const int group = t / (8 * g.tiles_n);
-  const int first_m = group * 8;
-  const int gsz = min(g.tiles_m - first_m, 8);
-  const int tm = first_m + (t % (8 * g.tiles_n)) % gsz;
-  const int tn = (t % (8 * g.tiles_n)) / gsz;
+  const int group = t / (GR * g.tiles_n);
+  const int first_m = group * GR;
+  const int gsz = min(g.tiles_m - first_m, GR);
+  const int tm = first_m + (t % (GR * g.tiles_n)) % gsz;
+  const int tn = (t % (GR * g.tiles_n)) / gsz;
   m0 = tm * BM;
   n0 = tn * BN;
 }
@@ -408,19 +411,19 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   int m0, n0;
-  tile_origin<P::BM, P::BN>(g, m0, n0);
+  tile_origin<P::BM, P::BN, (A_KM && !B_KM && !ACC) ? 4 : 8>(g, m0, n0);
   const int split = blockIdx.z;
   const int nkt = (g.K + BK - 1) / BK;
   const int kt0 = split * g.kt_per_split;
   const int nk = min(nkt, kt0 + g.kt_per_split) - kt0;
   // The k tiles are walked from a starting point that depends on the XCD (blocks are dealt to
   // the XCDs round-robin): stage j of this split (0 <= j < nk) is k tile kmap(j), a rotation by
-  // an eighth of the split per XCD.  Without it every workgroup of the chip loads the same k
+  // (3x mod 8) eighths of the split on XCD x (the permutation measured 1 % ahead of x eighths).  Without it every workgroup of the chip loads the same k
   // column of its rows at the same time; with rows a power of two apart in HBM (K = 2048 or 8192
   // bf16), those loads pile onto the same memory channels.  The workgroups of one XCD keep one
   // phase, so the operand panels they share in that XCD's L2 are still loaded once.  Each tile
   // keeps one fixed k order, so results stay deterministic.
-  const int rot = ((int(blockIdx.x) % kXCD) * nk) / kXCD;
+  const int rot = ((((int(blockIdx.x) % kXCD) * 3) % kXCD) * nk) / kXCD;
   auto kmap = [&](int j) { const int x = j + rot; return kt0 + (x >= nk ? x - nk : x); };
 
   const i32x4 ra = rsrc(g.a, g.a_bytes), rb = rsrc(g.b, g.b_bytes);
