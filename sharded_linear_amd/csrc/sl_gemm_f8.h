@@ -29,12 +29,13 @@ int f8_accum(hipStream_t st, F8Args g);
 // bf16 out[r][c] = E4M3(codes[r][c]) * 2^(scales[r][c/32] - 127); cols a multiple of 32
 int mx_dequant(hipStream_t st, const uint8_t* codes, const uint8_t* scales, void* out, int64_t rows, int64_t cols);
 
+// NVFP4 -> bf16 products E2M1 x E4M3 (exact; the tensor scale is not applied): q [rows][cols/2]
+// packed codes, s [rows][cols/16] scales, w [rows][cols] bf16; cols % 16 == 0, q and w 16-aligned.
+int nvfp4_expand(hipStream_t st, const uint8_t* q, const uint8_t* s, void* w, int64_t rows, int64_t cols);
+
 // MX quantisation of a bf16 matrix x[R][C] (row-major): rowwise codes qr[R][C] / scales
 // sr[R][C/32] (blocks of 32 along C) and/or columnwise codes qc[C][R] / scales sc[C][R/32]
 // (blocks of 32 along R, stored transposed).  Null outputs are skipped.  C % 32 == 0 for the
 // rowwise copy; R % 32 == 0 and C % 8 == 0 for the columnwise one.
-// NVFP4 -> bf16 products E2M1 x E4M3 (exact; the tensor scale is not applied): q [rows][cols/2]
-// packed codes, s [rows][cols/16] scales, w [rows][cols] bf16; cols % 16 == 0, q and w 16-aligned.
-int nvfp4_expand(hipStream_t st, const uint8_t* q, const uint8_t* s, void* w, int64_t rows, int64_t cols);
 int mx_quantize(hipStream_t st, const void* x, int64_t R, int64_t C, uint8_t* qr, uint8_t* sr, uint8_t* qc,
                 uint8_t* sc);
