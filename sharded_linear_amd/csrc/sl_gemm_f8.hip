@@ -176,8 +176,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
   const i32x4 rsa = rsrc(g.sa, g.sa_bytes), rsb = rsrc(g.sb, g.sb_bytes);
 
   // A stage's loads go out in two halves, A's at the top of the stage (right after the barrier
-  // that frees its slot) and B's before the stage's second k64 step, so they do not arrive at the
-  // texture-address queue in one burst (measured 3-5 % ahead of issuing both at the top).
+  // that frees its slot) and B's after the stage's first row of MFMAs.
   auto issue = [&](int kt, int slot) {
     char* base = smem + slot * kStage;
     const int k0 = kt * kF8RowBytes;
@@ -255,24 +254,42 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) scb[j] = TB::scales(lsb, wn * WN + j * 32, lane);
     }
+    // The stage's two k64 steps as 2 TM rows u = ks * TM + i of TN MFMAs each, in a fixed order:
+    // row u runs while A fragment u + 2 is read (and, two rows before step 1, step 1's B
+    // fragments), so a wave waits on LDS once per stage, for the first rows' fragments, instead of
+    // before nearly every row as the compiler's own order did (it kept one A fragment live).  B's
+    // code loads for the stage S - 1 ahead go out after row 0: measured 0.8-1.0 % ahead on the
+    // all-MXFP8 step of the previous order, where A's loads moved after row 0 lost 3.7 % and B's
+    // at the top tied.  Every accumulator still takes its k steps in order.
+    constexpr int NU = 2 * TM;
+    static_assert(TM >= 2, "rows per k64 step");
+    i32x8 fa[NU], fb[2][TN];
 #pragma unroll
-    for (int ks = 0; ks < kF8RowBytes / 64; ++ks) {
-      if (ks == 1) {
+    for (int j = 0; j < TN; ++j) fb[0][j] = TB::frag(lb, wn * WN + j * 32, 0, lane);
+    fa[0] = TA::frag(la, wm * WM, 0, lane);
+    fa[1] = TA::frag(la, wm * WM + 32, 0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int ks = u / TM, i = u % TM;
+      const int sh = 8 * (2 * ks + (lane >> 5));
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fb[ks][j], fa[u], acc[i][j], 0, 0, 0, int((scb[j] >> sh) & 0xFFu), 0, int((sca[i] >> sh) & 0xFFu));
+      if (u + 2 < NU) {
+        const int v = u + 2;
+        if (v == TM) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) fb[1][j] = TB::frag(lb, wn * WN + j * 32, 1, lane);
+        }
+        fa[v] = TA::frag(la, wm * WM + (v % TM) * 32, v / TM, lane);
+      }
+      if (u == 0) {
         const int nxt = it + S - 1;
         issue_b(kt0 + (nxt < nk ? nxt : nk), nxt % S);
       }
-      const int sh = 8 * (2 * ks + (lane >> 5));
-      i32x8 fa[TM], fb[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = TA::frag(la, wm * WM + i * 32, ks, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = TB::frag(lb, wn * WN + j * 32, ks, lane);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fb[j], fa[i], acc[i][j], 0, 0, 0, int((scb[j] >> sh) & 0xFFu), 0, int((sca[i] >> sh) & 0xFFu));
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   wait_vmcnt<0>();
