@@ -418,11 +418,11 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
   const int nk = min(nkt, kt0 + g.kt_per_split) - kt0;
   // The k tiles are walked from a starting point that depends on the XCD (blocks are dealt to
   // the XCDs round-robin): stage j of this split (0 <= j < nk) is k tile kmap(j), a rotation by
-  // (3x mod 8) eighths of the split on XCD x (the permutation measured 1 % ahead of x eighths).  Without it every workgroup of the chip loads the same k
-  // column of its rows at the same time; with rows a power of two apart in HBM (K = 2048 or 8192
-  // bf16), those loads pile onto the same memory channels.  The workgroups of one XCD keep one
-  // phase, so the operand panels they share in that XCD's L2 are still loaded once.  Each tile
-  // keeps one fixed k order, so results stay deterministic.
+  // (3x mod 8) eighths of the split on XCD x (measured 1 % ahead of x eighths).  Without it every
+  // workgroup of the chip loads the same k column of its rows at the same time; with rows a power
+  // of two apart in HBM (K = 2048 or 8192 bf16), those loads pile onto the same memory channels.
+  // The workgroups of one XCD keep one phase, so the operand panels they share in that XCD's L2
+  // are still loaded once.  Each tile keeps one fixed k order, so results stay deterministic.
   const int rot = ((((int(blockIdx.x) % kXCD) * 3) % kXCD) * nk) / kXCD;
   auto kmap = [&](int j) { const int x = j + rot; return kt0 + (x >= nk ? x - nk : x); };
 
