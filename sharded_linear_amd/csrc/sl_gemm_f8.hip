@@ -258,9 +258,9 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
     // row u runs while A fragment u + 2 is read (and, two rows before step 1, step 1's B
     // fragments), so a wave waits on LDS once per stage, for the first rows' fragments, instead of
     // before nearly every row as the compiler's own order did (it kept one A fragment live).  B's
-    // code loads for the stage S - 1 ahead go out after row 0: measured 0.8-1.0 % ahead on the
-    // all-MXFP8 step of the previous order, where A's loads moved after row 0 lost 3.7 % and B's
-    // at the top tied.  Every accumulator still takes its k steps in order.
+    // code loads for the stage S - 1 ahead go out after row 0.  Against the previous order this
+    // measured 0.5-1.0 % ahead on the all-MXFP8 step; with it, A's loads moved after row 0 lost
+    // 3.7 % and B's at the top tied.  Every accumulator still takes its k steps in order.
     constexpr int NU = 2 * TM;
     static_assert(TM >= 2, "rows per k64 step");
     i32x8 fa[NU], fb[2][TN];
