@@ -165,9 +165,9 @@ struct OpSel<false, R, BK, SW> { using T = MNMaj<R, BK, SW>; };
 // Workgroup -> macro-tile: blocks are dealt round-robin to the XCDs, so the block id is first
 // remapped to make each XCD's blocks a contiguous run of tile ids; tile ids then walk groups of
 // GR tile rows column by column, so the tiles one XCD runs at a time share A and B panels in its
-// L2.  GR is 8, or 4 for the dgrad kernels (there measured 3.6 % faster on c2's shapes: an XCD's
-// 32 tiles then take 4 rows of dY panels, which no other XCD of the round reads, and 8 columns
-// of W panels).
+// L2.  The fixed-order kernels take GR = 4 (an XCD's 32 tiles then span 4 tile rows and 8
+// columns): against 8 it measured 3.6 % faster on the dgrad of the Llama-3.2-1B MLP shard and
+// 0.3-1.5 % on the other products there and on the 7B layer shard; 2 and 16 were slower.
 template <int BM, int BN, int GR = 8>
 __device__ __forceinline__ void tile_origin(const Gemm2Args& g, int& m0, int& n0) {
   const int ntiles = g.tiles_m * g.tiles_n;
@@ -411,7 +411,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   int m0, n0;
-  tile_origin<P::BM, P::BN, (A_KM && !B_KM && !ACC) ? 4 : 8>(g, m0, n0);
+  tile_origin<P::BM, P::BN, 4>(g, m0, n0);
   const int split = blockIdx.z;
   const int nkt = (g.K + BK - 1) / BK;
   const int kt0 = split * g.kt_per_split;
