@@ -61,6 +61,9 @@ def parse():
                    help="skip the second pass that times every launch with HIP events")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES (reference for HBM byte counters)")
+    p.add_argument("--vendor-compare", action="store_true",
+                   help="only time the bf16 forward and dgrad against torch's library GEMMs on the "
+                        "workload's shapes (context for the per-kernel figures; not the step)")
     return p.parse_args()
 
 
@@ -107,6 +110,54 @@ def copy_calibration(nbytes: int) -> None:
     print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
 
 
+def vendor_compare(w, steps: int) -> None:
+    """Context for the per-kernel figures: the library's bf16 forward and dgrad beside torch's own
+    GEMMs on the same shapes (F.linear and matmul, hipBLASLt on ROCm), called in turn with the
+    operands rotating over 8 sets so that no call finds its inputs in the caches of the previous
+    one, HIP events around every call; one JSON line per shard with the medians.  The library
+    GEMMs are timed here only; the step never calls them."""
+    import torch
+    import torch.nn.functional as F
+
+    import sharded_linear_amd as sl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev).manual_seed(2024)
+    sets, T = 8, w.tokens
+    for n in w.step_params:
+        o, i = w.params[n]
+        rnd = lambda shape, std=1.0: (torch.randn(shape, device=dev, generator=gen) * std).to(torch.bfloat16)
+        Xs = [rnd((T, i)) for _ in range(sets)]
+        Ws = [rnd((o, i), 0.02) for _ in range(sets)]
+        dYs = [rnd((T, o)) for _ in range(sets)]
+        Y = torch.empty((T, o), dtype=torch.bfloat16, device=dev)
+        dX = torch.empty((T, i), dtype=torch.bfloat16, device=dev)
+        fns = {"fwd": lambda j: sl.sl_linear_fwd(Xs[j], Ws[j], Y),
+               "fwd_library": lambda j: F.linear(Xs[j], Ws[j]),
+               "dgrad": lambda j: sl.sl_linear_dgrad(dYs[j], Ws[j], dX),
+               "dgrad_library": lambda j: torch.matmul(dYs[j], Ws[j])}
+        for j in range(sets):
+            for f in fns.values():
+                f(j)
+        torch.cuda.synchronize()
+        ev = {k: [] for k in fns}
+        for r in range(steps):
+            for k, f in fns.items():
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                f(r % sets)
+                e.record()
+                ev[k].append((s, e))
+        torch.cuda.synchronize()
+        flops = 2 * T * i * o
+        rec = {"vendor_compare": n, "T_in_out": [T, i, o], "calls": steps}
+        for k, v in ev.items():
+            us = sorted(s.elapsed_time(e) * 1e3 for s, e in v)[len(v) // 2]
+            rec[k] = {"median_us": round(us, 2), "tflops": round(flops / us / 1e6, 1)}
+        print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -116,6 +167,10 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.vendor_compare:
+        from synth import configs
+        vendor_compare(configs.WORKLOADS[args.config], max(args.steps, 20))
         return
 
     import numpy as np
