@@ -458,7 +458,8 @@ Plan make_plan(Kind kind, bool mxfp8, int64_t M, int64_t N, int64_t K, int64_t a
     if (cfg == 10) cfg = 21;
     // A weight gradient whose 256x256 tiles cover about half of the 256 CUs, but whose 256x128
     // tiles make one full round, runs those unsplit on the 32x32x16 fixed-order kernel (cfg 20):
-    // 5 % ahead of two K splits plus the reduce (config 2 fc2).
+    // ahead of two K splits plus the reduce on the 1B MLP shard's down projection (main_grad
+    // [2048, 4096] over 8192 tokens), by 5 % and, against later forms of cfg 21, 0.4-0.6 %.
     if (kind == Kind::Wgrad && cfg == 21) {
       const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256), t128 = ((M + 255) / 256) * ((N + 127) / 128);
       if (t256 <= 144 && t128 >= 240 && t128 <= 288) cfg = 20;
