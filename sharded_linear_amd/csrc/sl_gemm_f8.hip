@@ -300,44 +300,43 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
 
 // bf16 out[r][c] = E4M3(codes[r][c]) * 2^(scales[r][c/32] - 127).  Rows hold whole 32-element
 // blocks and the scales one byte per block in the same order, so the arrays are linear in the
-// block index: 16-element chunk i is codes[16i, 16i+16), scale byte i/2 and out[16i, 16i+16), with
-// no row or column arithmetic.  Each thread keeps two chunks in flight (the kernel is bound by HBM
-// bytes, 3 per element).  The product is formed by v_cvt_scalef32_pk_bf16_fp8 with the scale as an
-// fp32 power of two; it is exact whenever the result is a normal bf16, which the entry points
-// require.
+// block index: 8-element chunk i is codes[8i, 8i+8), scale byte i/4 and out[8i, 8i+8), with no
+// row or column arithmetic.  A lane's chunk leaves as one 16-byte store, so every store
+// instruction of a wave covers 1 KiB contiguously (0.6-0.9 % ahead on the MXFP8-operand step of
+// 16-element chunks stored as two halves 32 bytes apart).  Each thread keeps four chunks in
+// flight (the kernel is bound by HBM bytes, 3 per element).  The product is formed by
+// v_cvt_scalef32_pk_bf16_fp8 with the scale as an fp32 power of two; it is exact whenever the
+// result is a normal bf16, which the entry points require.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   if (s == 0xFFu) return __builtin_bit_cast(float, 0x7FC00000u);             // NaN scale
   return s ? __builtin_bit_cast(float, s << 23) : __builtin_bit_cast(float, 0x00400000u);  // 2^-127
 }
 
-__global__ void __launch_bounds__(256) mx_dequant_bf16(const uint4* codes, const uint8_t* scales, uint4* out,
-                                                       int64_t n16) {
-  constexpr int U = 2;
+__global__ void __launch_bounds__(256) mx_dequant_bf16(const uint2* codes, const uint8_t* scales, uint4* out,
+                                                       int64_t n8) {
+  constexpr int U = 4;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t base = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; base < n16; base += U * stride) {
-    uint4 q[U];
+  for (int64_t base = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; base < n8; base += U * stride) {
+    uint2 q[U];
     float sc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + u * stride;
-      if (i < n16) {
+      if (i < n8) {
         q[u] = codes[i];
-        sc[u] = e8m0_to_f32(scales[i >> 1]);
+        sc[u] = e8m0_to_f32(scales[i >> 2]);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + u * stride;
-      if (i < n16) {
-        const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-        uint32_t o[8];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          o[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], sc[u], false));
-          o[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[h], sc[u], true));
-        }
-        out[2 * i] = make_uint4(o[0], o[1], o[2], o[3]);
-        out[2 * i + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+      if (i < n8) {
+        uint32_t o[4];
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[u].x, sc[u], false));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[u].x, sc[u], true));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[u].y, sc[u], false));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[u].y, sc[u], true));
+        out[i] = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
   }
@@ -385,11 +384,11 @@ int f8_accum(hipStream_t st, F8Args g) {
 }
 
 int mx_dequant(hipStream_t st, const uint8_t* codes, const uint8_t* scales, void* out, int64_t rows, int64_t cols) {
-  const int64_t n16 = rows * (cols / 16);
-  if (n16 == 0) return 0;
-  int64_t blocks = (n16 + 511) / 512;          // 256 threads x 2 chunks each
+  const int64_t n8 = rows * (cols / 8);
+  if (n8 == 0) return 0;
+  int64_t blocks = (n8 + 1023) / 1024;          // 256 threads x 4 chunks each
   if (blocks > 16384) blocks = 16384;
-  hipLaunchKernelGGL(sl2::mx_dequant_bf16, dim3(unsigned(blocks)), dim3(256), 0, st, reinterpret_cast<const uint4*>(codes),
-                     scales, static_cast<uint4*>(out), n16);
+  hipLaunchKernelGGL(sl2::mx_dequant_bf16, dim3(unsigned(blocks)), dim3(256), 0, st, reinterpret_cast<const uint2*>(codes),
+                     scales, static_cast<uint4*>(out), n8);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
