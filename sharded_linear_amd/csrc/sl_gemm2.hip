@@ -526,8 +526,12 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1) gemm4(Gemm2Args g) {
   // step, one every NQ/NL MFMAs, which keeps the texture-address queue from filling.
   auto step = [&](auto ic_cur, auto ic_nm, auto&& mem) {
     constexpr int cur = decltype(ic_cur)::value, NM = decltype(ic_nm)::value;
+    // MFMAs row by row over the A fragments, the B fragments in serpentine order (odd rows run j
+    // backwards), so that every MFMA shares an operand with the one before it: the part is held
+    // at its power limit, and fewer operand changes measured 0.3-0.6 % faster per launch on every
+    // product.
     static_for<TM * TN>([&](auto qc) {
-      constexpr int q = decltype(qc)::value, i = q / TN, j = q % TN;
+      constexpr int q = decltype(qc)::value, i = q / TN, j = (i & 1) ? TN - 1 - q % TN : q % TN;
       if constexpr (MF == 32)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
       else

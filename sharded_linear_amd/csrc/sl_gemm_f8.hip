@@ -273,10 +273,13 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_f8fwd(F8Args g) {
     for (int u = 0; u < NU; ++u) {
       const int ks = u / TM, i = u % TM;
       const int sh = 8 * (2 * ks + (lane >> 5));
+      // odd rows run j backwards, so every MFMA shares an operand with the one before it
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int jj = 0; jj < TN; ++jj) {
+        const int j = (u & 1) ? TN - 1 - jj : jj;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             fb[ks][j], fa[u], acc[i][j], 0, 0, 0, int((scb[j] >> sh) & 0xFFu), 0, int((sca[i] >> sh) & 0xFFu));
+      }
       if (u + 2 < NU) {
         const int v = u + 2;
         if (v == TM) {
